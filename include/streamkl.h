@@ -1,0 +1,124 @@
+/*
+ * streamkl.h - C ABI of the StreamKL engine for AMD Instinct MI355X (gfx950).
+ *
+ * StreamKL computes, for every query row i of every (batch, head) slice, the KL divergence
+ * KL(P1 || P2)[i] between two attention distributions P_t = softmax(scale * Q_t K_t^T) over the
+ * keys, without ever forming an N_Q x N_K matrix, and the gradients of sum_i g_i * KL[i] in
+ * two settings. Sources: "StreamKL: Fast and Memory-Efficient KL Divergence for Boosting
+ * Attention Distillation" as summarised on gist.science/pt/paper/2606.20005 ("Definicao do
+ * Problema"; "Metodologia" sections 1-3) and gist.science/hi/paper/2606.20005 (technical
+ * summary, same sections).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors q1, q2 are [batch, heads, n_q, head_dim] and k1, k2 are [batch, heads, n_k,
+ *    head_dim], bfloat16, in device memory, addressed through the element strides of
+ *    streamkl_problem_t (the head_dim axis is contiguous). All pointers must be 16-byte aligned
+ *    and every stride a multiple of 8 elements.
+ *  - Causal masking is top-left: key j is visible to query i iff j <= i. Every row then has at
+ *    least one visible key.
+ *  - Logits are S_t = scale * Q_t K_t^T; LSE values use the natural logarithm.
+ *  - The caller owns every buffer. The library never allocates, frees or synchronises device
+ *    memory; every call enqueues kernels on `stream` and returns without waiting. Buffers must
+ *    stay valid until the stream has executed the work. There is no global mutable state apart
+ *    from a thread-local error message, so calls from several host threads are safe.
+ *  - Validation happens before anything is enqueued: an invalid call returns an error status
+ *    and touches no buffer. A launch failure returns STREAMKL_ERROR_HIP; outputs are then
+ *    undefined. Non-finite inputs are not checked; they propagate.
+ *  - Inputs may alias each other (k2 == k1 and/or q2 == q1 are allowed and k2 == k1 is
+ *    detected and loads the shared tensor once). Outputs must not overlap any input or each
+ *    other (STREAMKL_ERROR_INVALID_VALUE).
+ */
+#ifndef STREAMKL_H
+#define STREAMKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STREAMKL_SUCCESS = 0,
+  STREAMKL_ERROR_INVALID_VALUE = 1, /* bad pointer, size, stride, alignment or overlap */
+  STREAMKL_ERROR_NOT_SUPPORTED = 2, /* valid but unsupported (head_dim not 64 or 128) */
+  STREAMKL_ERROR_HIP = 3            /* the HIP runtime reported an error (no device, launch) */
+} streamkl_status_t;
+
+typedef struct {
+  int64_t batch;        /* >= 1 */
+  int64_t heads;        /* >= 1 */
+  int64_t n_q;          /* query rows per slice, >= 1 */
+  int64_t n_k;          /* key rows per slice, >= 1 */
+  int64_t head_dim;     /* 64 or 128 */
+  int64_t q_stride[3];  /* element strides of (batch, head, row) for q1 and q2 */
+  int64_t k_stride[3];  /* element strides of (batch, head, row) for k1 and k2 */
+  float scale;          /* logit scale, finite and > 0 (1/sqrt(head_dim) is usual) */
+  int32_t causal;       /* 0: every key visible; 1: top-left causal mask */
+} streamkl_problem_t;
+
+/*
+ * Forward pass (gist.science/pt "Metodologia" section 1, "Formulacao Online"; saved state per
+ * section 2, "Estado Salvo").
+ *
+ * Streams key tiles through on-chip memory and keeps per query row the running maxima m1, m2,
+ * the running sums of exponentials l1, l2 and the P1-weighted logit-difference accumulator acc,
+ * rescaled whenever a running maximum grows; then writes
+ *     lse_t[i] = m_t + log l_t,      kl[i] = acc / l1 + lse2[i] - lse1[i].
+ * Outputs (device, float32, contiguous [batch, heads, n_q], overwritten): kl, lse1, lse2.
+ * The result is bitwise deterministic, and kl is exactly 0 where (Q1, K1) and (Q2, K2) hold
+ * identical values.
+ */
+streamkl_status_t streamkl_fwd(const streamkl_problem_t* problem,
+                               const void* q1, const void* k1, const void* q2, const void* k2,
+                               float* kl, float* lse1, float* lse2, hipStream_t stream);
+
+/*
+ * Backward, setting 1: P1 fixed (stop-gradient), P2 free - standard distillation
+ * (gist.science/pt "Metodologia" section 2, "Configuracao 1").
+ *
+ * Regenerates P_t = exp(S_t - lse_t) tile by tile from the saved lse1, lse2 and the inputs,
+ * forms dS2 = g_i * (P2 - P1) and writes the gradients of sum_i g_i * KL[i] w.r.t. Q2 and K2:
+ *     dq2 = scale * dS2 K2,   dk2 = scale * dS2^T Q2.
+ * lse1, lse2, grad_kl: device float32 contiguous [batch, heads, n_q]; lse_t as written by
+ * streamkl_fwd for the same inputs. grad_kl holds g_i (any real values).
+ * Outputs dq2 [batch, heads, n_q, head_dim] and dk2 [batch, heads, n_k, head_dim]: device
+ * bfloat16, contiguous, overwritten; accumulation is float32. With k2 == k1, dk2 is the
+ * gradient through the student side only. Deterministic (no atomics).
+ */
+streamkl_status_t streamkl_bwd_fixP1(const streamkl_problem_t* problem,
+                                     const void* q1, const void* k1, const void* q2,
+                                     const void* k2, const float* lse1, const float* lse2,
+                                     const float* grad_kl, void* dq2, void* dk2,
+                                     hipStream_t stream);
+
+/*
+ * Backward, setting 2: P2 fixed (stop-gradient), P1 free (gist.science/pt "Metodologia"
+ * section 2, "Configuracao 2"; the log-ratio follows section 3, "Estabilidade Numerica").
+ *
+ * Forms dS1 = g_i * P1 * (log P1 - log P2 - KL[i]) with the log-ratio taken from logit
+ * differences and saved LSEs, (S1 - lse1) - (S2 - lse2), never from the log of a probability,
+ * and writes  dq1 = scale * dS1 K1,  dk1 = scale * dS1^T Q1.
+ * kl: the forward's saved KL, device float32 contiguous [batch, heads, n_q]; other arguments
+ * as in streamkl_bwd_fixP1. Outputs dq1, dk1: device bfloat16, contiguous, overwritten.
+ */
+streamkl_status_t streamkl_bwd_fixP2(const streamkl_problem_t* problem,
+                                     const void* q1, const void* k1, const void* q2,
+                                     const void* k2, const float* lse1, const float* lse2,
+                                     const float* kl, const float* grad_kl, void* dq1, void* dk1,
+                                     hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* streamkl_status_string(streamkl_status_t status);
+
+/* Detail of the last failed call on the calling host thread ("" if none). Valid until the
+ * next call on that thread. */
+const char* streamkl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMKL_H */

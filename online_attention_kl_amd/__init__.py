@@ -1,0 +1,174 @@
+"""StreamKL for AMD Instinct MI355X: a thin Python binding of libstreamkl.so.
+
+The binding only marshals arguments: it checks shapes and dtypes, allocates outputs with
+PyTorch (device memory is PyTorch's job) and passes raw pointers and the current HIP stream to
+the C ABI declared in include/streamkl.h. Every step of the computation runs in the library's
+HIP kernels; there is no fallback. If the library has not been built, `lib()` raises.
+
+Functions (names follow the C ABI):
+  streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False)           -> (kl, lse1, lse2)
+  streamkl_bwd_fixP1(q1, k1, q2, k2, lse1, lse2, grad_kl, ...)      -> (dq2, dk2)
+  streamkl_bwd_fixP2(q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...)  -> (dq1, dk1)
+Inputs are bfloat16 CUDA tensors [B, H, N, d] (the d axis contiguous, any other strides that
+are multiples of 8 elements); kl / lse / grad_kl are float32 [B, H, N_Q].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamkl.so")
+
+STATUS = {0: "STREAMKL_SUCCESS", 1: "STREAMKL_ERROR_INVALID_VALUE",
+          2: "STREAMKL_ERROR_NOT_SUPPORTED", 3: "STREAMKL_ERROR_HIP"}
+
+EXPORTS = ("streamkl_fwd", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2",
+           "streamkl_status_string", "streamkl_last_error")
+
+
+class StreamKLError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("n_q", ctypes.c_int64),
+                ("n_k", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib(path: str | None = None) -> ctypes.CDLL:
+    """Load libstreamkl.so (once). Raises if it is missing: there is no fallback path."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"libstreamkl.so not found at {p}; build it with "
+                          "`python -m online_attention_kl_amd.build`")
+    L = ctypes.CDLL(p)
+    vp, fp = ctypes.c_void_p, ctypes.c_void_p
+    pp = ctypes.POINTER(Problem)
+    L.streamkl_fwd.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp]
+    L.streamkl_bwd_fixP1.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp, vp, vp]
+    L.streamkl_bwd_fixP2.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, fp, vp, vp, vp]
+    for name in ("streamkl_fwd", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2"):
+        getattr(L, name).restype = ctypes.c_int
+    L.streamkl_status_string.argtypes = [ctypes.c_int]
+    L.streamkl_status_string.restype = ctypes.c_char_p
+    L.streamkl_last_error.argtypes = []
+    L.streamkl_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        msg = lib().streamkl_last_error().decode()
+        raise StreamKLError(status, msg)
+
+
+def make_problem(q1, k1, scale, causal) -> Problem:
+    B, H, nq, d = q1.shape
+    nk = k1.shape[2]
+    p = Problem()
+    p.batch, p.heads, p.n_q, p.n_k, p.head_dim = B, H, nq, nk, d
+    for i in range(3):
+        p.q_stride[i] = q1.stride(i)
+        p.k_stride[i] = k1.stride(i)
+    p.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    p.causal = 1 if causal else 0
+    return p
+
+
+def _check_inputs(q1, k1, q2, k2):
+    import torch
+    for name, t in (("q1", q1), ("k1", k1), ("q2", q2), ("k2", k2)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be a bfloat16 CUDA tensor [B, H, N, d] with a "
+                             "contiguous last dimension")
+    if q1.shape != q2.shape or q1.stride() != q2.stride():
+        raise ValueError("q1 and q2 must have the same shape and strides")
+    if k1.shape != k2.shape or k1.stride() != k2.stride():
+        raise ValueError("k1 and k2 must have the same shape and strides")
+    if k1.shape[:2] != q1.shape[:2] or k1.shape[3] != q1.shape[3]:
+        raise ValueError("q and k must agree on batch, heads and head_dim")
+
+
+def _rowvec(t, name, shape):
+    import torch
+    if not t.is_cuda or t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape {shape}")
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False, out=None):
+    """Per-row KL(P1 || P2), LSE1, LSE2 (float32 [B, H, N_Q])."""
+    import torch
+    _check_inputs(q1, k1, q2, k2)
+    B, H, nq, _ = q1.shape
+    if out is None:
+        out = tuple(torch.empty((B, H, nq), dtype=torch.float32, device=q1.device)
+                    for _ in range(3))
+    for n, t in zip(("kl", "lse1", "lse2"), out):
+        _rowvec(t, n, (B, H, nq))
+    p = make_problem(q1, k1, scale, causal)
+    _check(lib().streamkl_fwd(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
+                              k2.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
+                              out[2].data_ptr(), _stream(q1)))
+    return out
+
+
+def _grad_out(q, k, out):
+    import torch
+    if out is None:
+        out = (torch.empty(q.shape, dtype=torch.bfloat16, device=q.device),
+               torch.empty(k.shape, dtype=torch.bfloat16, device=k.device))
+    for n, t, ref in (("dq", out[0], q), ("dk", out[1], k)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.shape != ref.shape \
+                or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous bfloat16 CUDA tensor of shape {tuple(ref.shape)}")
+    return out
+
+
+def streamkl_bwd_fixP1(q1, k1, q2, k2, lse1, lse2, grad_kl, scale=None, causal=False, out=None):
+    """Setting 1 (P1 fixed): gradients (dq2, dk2) of sum g_i KL_i, bfloat16."""
+    _check_inputs(q1, k1, q2, k2)
+    B, H, nq, _ = q1.shape
+    for n, t in (("lse1", lse1), ("lse2", lse2), ("grad_kl", grad_kl)):
+        _rowvec(t, n, (B, H, nq))
+    out = _grad_out(q2, k2, out)
+    p = make_problem(q1, k1, scale, causal)
+    _check(lib().streamkl_bwd_fixP1(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
+                                    k2.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
+                                    grad_kl.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
+                                    _stream(q1)))
+    return out
+
+
+def streamkl_bwd_fixP2(q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=None, causal=False,
+                       out=None):
+    """Setting 2 (P2 fixed): gradients (dq1, dk1) of sum g_i KL_i, bfloat16."""
+    _check_inputs(q1, k1, q2, k2)
+    B, H, nq, _ = q1.shape
+    for n, t in (("lse1", lse1), ("lse2", lse2), ("kl", kl), ("grad_kl", grad_kl)):
+        _rowvec(t, n, (B, H, nq))
+    out = _grad_out(q1, k1, out)
+    p = make_problem(q1, k1, scale, causal)
+    _check(lib().streamkl_bwd_fixP2(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
+                                    k2.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
+                                    kl.data_ptr(), grad_kl.data_ptr(), out[0].data_ptr(),
+                                    out[1].data_ptr(), _stream(q1)))
+    return out

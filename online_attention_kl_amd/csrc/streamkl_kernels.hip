@@ -1,0 +1,782 @@
+// StreamKL kernels for gfx950 (AMD Instinct MI355X) and the C ABI declared in streamkl.h.
+//
+// What is computed (gist.science/pt/paper/2606.20005, "Metodologia" sections 1-3):
+//   per (batch, head) slice and query row i, with S_t = scale * Q_t K_t^T,
+//   forward:  five running per-row scalars m1, l1, m2, l2, acc over streamed key tiles, then
+//             LSE_t = m_t + log l_t,  KL = acc / l1 + LSE2 - LSE1;
+//   backward: P_t = exp(S_t - LSE_t) regenerated tile by tile from the saved LSEs, then
+//             setting 1 (P1 fixed): dS2 = g (P2 - P1);
+//             setting 2 (P2 fixed): dS1 = g P1 ((S1 - LSE1) - (S2 - LSE2) - KL)
+//             and dQ_f = scale dS K_f, dK_f = scale dS^T Q_f for the free side f.
+//
+// Design (MI355X-first; the pages' own kernels target NVIDIA parts and are prior art only):
+//  * All contractions run on v_mfma_f32_32x32x16_bf16 (bf16 in, fp32 accumulate), one wave64
+//    per 32x32 output tile.
+//  * The forward and the dQ kernel are query-major: a wave keeps the B operand fragments of its
+//    32 query rows of Q1 and Q2 in registers for the whole kernel and computes S^T = K Q^T, so
+//    each lane owns one query row and 16 of the keys of every 32-key block. Each lane then keeps
+//    its own partial online state (m1, l1, m2, l2, acc) with no cross-lane traffic in the hot
+//    loop; the two lanes that share a query merge their states once at the end (the merge of
+//    two partial states is associative). The P1-weighted logit difference is accumulated from
+//    the unscaled dot products and scaled once at the end.
+//  * The dK kernel is key-major: a wave keeps its 32 key rows of K1 and K2 in registers and
+//    computes S = Q K^T, so dS^T comes out of the accumulator already in the A-operand layout
+//    of dK = dS^T Q. Symmetrically, the dQ kernel's dS is the A operand of dQ = dS K. The other
+//    operand of each gradient GEMM is read from the row-major LDS tile with
+//    ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit values across lanes, so no
+//    transposed copy is ever stored. The two backward kernels recompute S independently and
+//    never use atomics: results are deterministic.
+//  * Streamed tiles are staged in LDS with a 16-byte-chunk XOR swizzle (chunk ^ row) so that
+//    the 32 rows read by one MFMA operand load fall in distinct banks.
+//  * exp and log use the hardware base-2 instructions; scale * log2(e) is folded into one FMA
+//    per element and the saved LSEs stay in natural-log units.
+//  * Causal (top-left) masking skips whole tiles past the frontier; only tiles that straddle
+//    the diagonal or the ragged end of a sequence take the masked path. Causal grids run the
+//    longest row blocks first, and block ids interleave the (batch, head) slices so that all
+//    blocks of one slice land on one XCD and share its L2.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/streamkl.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+constexpr int kThreads = 256;  // 4 waves of 64
+constexpr int kWaves = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1.0e30f;  // finite stand-in for -inf in running maxima
+constexpr float kInf = __builtin_huge_valf();
+
+struct Shape {
+  int nq, nk, bh, heads;
+  long long q_sb, q_sh, q_sr;
+  long long k_sb, k_sh, k_sr;
+  float scale;
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// Row (within a 32-row block) of accumulator register r of a 32x32 MFMA result for a lane in
+// half h (lanes 32..63 are h = 1). The lane's column is lane & 31.
+__device__ __forceinline__ int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
+
+__device__ __forceinline__ bf16x8 load_frag(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// Eight fp32 values -> bf16x8 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(v[i]);
+  return r;
+}
+
+// ---------------------------------------------------------------- LDS tiles
+// A tile of ROWS rows x D bf16 values, stored as 16-byte chunks; chunk c of row r lives at
+// chunk slot r * CPR + (c ^ (r % CPR)).
+template <int D>
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  constexpr int CPR = D / 8;
+  return (row * CPR + (chunk ^ (row & (CPR - 1)))) * 8;
+}
+
+template <int ROWS, int D>
+struct TileRegs {
+  static constexpr int CPR = D / 8;
+  static constexpr int N = ROWS * CPR / kThreads;
+  static_assert(N * kThreads == ROWS * CPR, "tile must split evenly over the block");
+  uint4 v[N];
+
+  // Rows row0.. of a [n_valid, D] matrix with row stride rstride; rows >= n_valid read as 0.
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, long long rstride,
+                                       int row0, int n_valid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = threadIdx.x + i * kThreads;
+      const int row = idx / CPR, c = idx % CPR;
+      const int gr = row0 + row;
+      if (gr < n_valid)
+        v[i] = *reinterpret_cast<const uint4*>(base + (long long)gr * rstride + c * 8);
+      else
+        v[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = threadIdx.x + i * kThreads;
+      const int row = idx / CPR, c = idx % CPR;
+      *reinterpret_cast<uint4*>(lds + lds_off<D>(row, c)) = v[i];
+    }
+  }
+};
+
+// A operand of a 32x32x16 MFMA: row `row` of the LDS tile, 8 values at columns
+// kk * 16 + h * 8 .. +8.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_a_frag(const uint16_t* lds, int row, int kk, int h) {
+  return load_frag(lds + lds_off<D>(row, kk * 2 + h));
+}
+
+// B operand [k = tile row, n = column] of a 32x32x16 MFMA read from a row-major LDS tile with
+// ds_read_b64_tr_b16. Lane l receives column colbase + (l & 31) and the 8 tile rows
+//   rowbase + (t / 4) * 8 + (l / 32) * 4 + (t % 4),  t = 0..7,
+// which is the order in which a 32x32 accumulator holds its rows (acc_row), so that an
+// accumulator's registers 8c..8c+7 form the matching A operand for rowbase = 16 c.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_bt_frag(const uint16_t* lds, int rowbase, int colbase) {
+  const int l = lane_id(), g = l >> 4, i = l & 15;
+  const int col = colbase + (g & 1) * 16 + 4 * (i & 3);
+  const int chunk = col >> 3, within = col & 7;
+  const lds_u16* base = (const lds_u16*)(lds);
+  s16x4 v[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = rowbase + 8 * j + (g >> 1) * 4 + (i >> 2);
+    const int off = lds_off<D>(row, chunk) + within;
+    v[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+  }
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// ---------------------------------------------------------------- block -> tile mapping
+// Block ids interleave slices: id = rank * n_slices + slice, so consecutive ids (which the
+// hardware deals round-robin to the 8 XCDs) are different slices and every block of one slice
+// shares the XCD (and L2) of that slice when n_slices is a multiple of 8.
+__device__ __forceinline__ void block_coords(int n_slices, int& rank, int& slice) {
+  rank = blockIdx.x / n_slices;
+  slice = blockIdx.x - rank * n_slices;
+}
+
+// ================================================================ forward
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void fwd_tile_update(const f32x16 (&s1)[2], const f32x16 (&s2)[2],
+                                                float c, int key0, int query, int nk, int h,
+                                                float& m1, float& l1, float& m2, float& l2,
+                                                float& acc) {
+  float e1[32], e2[32], d12[32];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = rb * 16 + r;
+      e1[i] = s1[rb][r];
+      e2[i] = s2[rb][r];
+      d12[i] = e1[i] - e2[i];
+      if (MASK) {
+        const int key = key0 + rb * 32 + acc_row(r, h);
+        const bool ok = key < nk && (!CAUSAL || key <= query);
+        e1[i] = ok ? e1[i] : -kInf;
+        e2[i] = ok ? e2[i] : -kInf;
+      }
+    }
+  float mx1 = e1[0], mx2 = e2[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    mx1 = fmaxf(mx1, e1[i]);
+    mx2 = fmaxf(mx2, e2[i]);
+  }
+  const float m1n = fmaxf(m1, mx1), m2n = fmaxf(m2, mx2);
+  const float a1 = exp2_hw((m1 - m1n) * c), a2 = exp2_hw((m2 - m2n) * c);
+  const float nb1 = -m1n * c, nb2 = -m2n * c;
+  float sl1[4] = {0.f, 0.f, 0.f, 0.f}, sl2[4] = {0.f, 0.f, 0.f, 0.f}, sa[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float p1 = exp2_hw(fmaf(e1[i], c, nb1));
+    const float p2 = exp2_hw(fmaf(e2[i], c, nb2));
+    sl1[i & 3] += p1;
+    sl2[i & 3] += p2;
+    sa[i & 3] = fmaf(p1, d12[i], sa[i & 3]);
+  }
+  l1 = fmaf(l1, a1, (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]));
+  l2 = fmaf(l2, a2, (sl2[0] + sl2[1]) + (sl2[2] + sl2[3]));
+  acc = fmaf(acc, a1, (sa[0] + sa[1]) + (sa[2] + sa[3]));
+  m1 = m1n;
+  m2 = m2n;
+}
+
+template <int D, bool CAUSAL, bool SHARED_K>
+__global__ void __launch_bounds__(kThreads)
+fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
+           const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
+           float* __restrict__ kl_out, float* __restrict__ lse1_out,
+           float* __restrict__ lse2_out, Shape s) {
+  constexpr int BQ = 32 * kWaves, BK = 64, KS = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t lk1[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lk2[SHARED_K ? 8 : BK * D];
+
+  int rank, slice;
+  block_coords(s.bh, rank, slice);
+  const int nqb = (s.nq + BQ - 1) / BQ;
+  const int qb = CAUSAL ? nqb - 1 - rank : rank;
+  const int b = slice / s.heads, hd = slice - b * s.heads;
+  const uint16_t* Q1 = q1 + b * s.q_sb + hd * s.q_sh;
+  const uint16_t* Q2 = q2 + b * s.q_sb + hd * s.q_sh;
+  const uint16_t* K1 = k1 + b * s.k_sb + hd * s.k_sh;
+  const uint16_t* K2 = k2 + b * s.k_sb + hd * s.k_sh;
+
+  const int l = lane_id(), w = wave_id(), h = l >> 5, col = l & 31;
+  const int qw0 = qb * BQ + w * 32;
+  const int query = qw0 + col;
+  const int qrow = query < s.nq ? query : s.nq - 1;
+
+  bf16x8 f1[KS], f2[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    f1[kk] = load_frag(Q1 + (long long)qrow * s.q_sr + kk * 16 + h * 8);
+    f2[kk] = load_frag(Q2 + (long long)qrow * s.q_sr + kk * 16 + h * 8);
+  }
+
+  const int last_q = min(s.nq - 1, qb * BQ + BQ - 1);
+  const int kend = CAUSAL ? min(s.nk, last_q + 1) : s.nk;
+  const int ntiles = (kend + BK - 1) / BK;
+  const float c = s.scale * kLog2e;
+  const bool wave_live = qw0 < s.nq;
+
+  float m1 = kNegBig, m2 = kNegBig, l1 = 0.f, l2 = 0.f, acc = 0.f;
+  TileRegs<BK, D> r1, r2;
+  r1.load(K1, s.k_sr, 0, s.nk);
+  if (!SHARED_K) r2.load(K2, s.k_sr, 0, s.nk);
+
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    r1.store(lk1);
+    if (!SHARED_K) r2.store(lk2);
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      r1.load(K1, s.k_sr, (t + 1) * BK, s.nk);
+      if (!SHARED_K) r2.load(K2, s.k_sr, (t + 1) * BK, s.nk);
+    }
+    const int key0 = t * BK;
+    if (!wave_live) continue;
+    if (CAUSAL && key0 > qw0 + 31) continue;  // every key of the tile is past this wave's rows
+    f32x16 s1[2], s2[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      f32x16 x1 = {}, x2 = {};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const bf16x8 a = lds_a_frag<D>(lk1, rb * 32 + col, kk, h);
+        x1 = mfma(a, f1[kk], x1);
+        const bf16x8 a2 = SHARED_K ? a : lds_a_frag<D>(lk2, rb * 32 + col, kk, h);
+        x2 = mfma(a2, f2[kk], x2);
+      }
+      s1[rb] = x1;
+      s2[rb] = x2;
+    }
+    const bool full = (key0 + BK <= s.nk) && (!CAUSAL || key0 + BK - 1 <= qw0);
+    if (full)
+      fwd_tile_update<D, CAUSAL, false>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+    else
+      fwd_tile_update<D, CAUSAL, true>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+  }
+
+  // Merge the two partial states of this query row (lanes l and l ^ 32).
+  const float om1 = __shfl_xor(m1, 32), ol1 = __shfl_xor(l1, 32);
+  const float om2 = __shfl_xor(m2, 32), ol2 = __shfl_xor(l2, 32);
+  const float oacc = __shfl_xor(acc, 32);
+  if (h == 0 && query < s.nq) {
+    const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
+    const float fa = exp2_hw((m1 - M1) * c), fb = exp2_hw((om1 - M1) * c);
+    const float ga = exp2_hw((m2 - M2) * c), gb = exp2_hw((om2 - M2) * c);
+    const float L1 = l1 * fa + ol1 * fb;
+    const float L2 = l2 * ga + ol2 * gb;
+    const float A = acc * fa + oacc * fb;
+    const float lse1 = M1 * s.scale + log2_hw(L1) * kLn2;
+    const float lse2 = M2 * s.scale + log2_hw(L2) * kLn2;
+    const long long o = (long long)slice * s.nq + query;
+    kl_out[o] = s.scale * A / L1 + (lse2 - lse1);
+    lse1_out[o] = lse1;
+    lse2_out[o] = lse2;
+  }
+}
+
+// ================================================================ backward: dQ (query-major)
+template <int D, int SETTING, bool CAUSAL, bool SHARED_K>
+__global__ void __launch_bounds__(kThreads)
+dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
+          const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
+          const float* __restrict__ lse1, const float* __restrict__ lse2,
+          const float* __restrict__ klv, const float* __restrict__ gv,
+          __bf16* __restrict__ dq_out, Shape s) {
+  constexpr int BQ = 32 * kWaves, BT = 32, KS = D / 16, NB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t lk1[BT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lk2[SHARED_K ? 8 : BT * D];
+  __shared__ float gscale[kWaves][32];
+
+  int rank, slice;
+  block_coords(s.bh, rank, slice);
+  const int nqb = (s.nq + BQ - 1) / BQ;
+  const int qb = CAUSAL ? nqb - 1 - rank : rank;
+  const int b = slice / s.heads, hd = slice - b * s.heads;
+  const uint16_t* Q1 = q1 + b * s.q_sb + hd * s.q_sh;
+  const uint16_t* Q2 = q2 + b * s.q_sb + hd * s.q_sh;
+  const uint16_t* K1 = k1 + b * s.k_sb + hd * s.k_sh;
+  const uint16_t* K2 = k2 + b * s.k_sb + hd * s.k_sh;
+  const uint16_t* lkf = (SETTING == 1 && !SHARED_K) ? lk2 : lk1;  // free-side K tile
+
+  const int l = lane_id(), w = wave_id(), h = l >> 5, col = l & 31;
+  const int qw0 = qb * BQ + w * 32;
+  const int query = qw0 + col;
+  const int qrow = query < s.nq ? query : s.nq - 1;
+  const long long ro = (long long)slice * s.nq + qrow;
+
+  bf16x8 f1[KS], f2[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    f1[kk] = load_frag(Q1 + (long long)qrow * s.q_sr + kk * 16 + h * 8);
+    f2[kk] = load_frag(Q2 + (long long)qrow * s.q_sr + kk * 16 + h * 8);
+  }
+  const float c = s.scale * kLog2e;
+  const float b1 = -lse1[ro] * kLog2e;
+  const float b2 = -lse2[ro] * kLog2e;                                   // setting 1
+  const float cst = SETTING == 2 ? (lse2[ro] - lse1[ro]) - klv[ro] : 0.f;  // setting 2
+  if (h == 0) gscale[w][col] = gv[ro] * s.scale;
+
+  const int last_q = min(s.nq - 1, qb * BQ + BQ - 1);
+  const int kend = CAUSAL ? min(s.nk, last_q + 1) : s.nk;
+  const int ntiles = (kend + BT - 1) / BT;
+  const bool wave_live = qw0 < s.nq;
+
+  f32x16 dq[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) dq[nb] = f32x16{};
+
+  TileRegs<BT, D> r1, r2;
+  r1.load(K1, s.k_sr, 0, s.nk);
+  if (!SHARED_K) r2.load(K2, s.k_sr, 0, s.nk);
+
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    r1.store(lk1);
+    if (!SHARED_K) r2.store(lk2);
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      r1.load(K1, s.k_sr, (t + 1) * BT, s.nk);
+      if (!SHARED_K) r2.load(K2, s.k_sr, (t + 1) * BT, s.nk);
+    }
+    const int key0 = t * BT;
+    if (!wave_live) continue;
+    if (CAUSAL && key0 > qw0 + 31) continue;
+    f32x16 x1 = {}, x2 = {};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const bf16x8 a = lds_a_frag<D>(lk1, col, kk, h);
+      x1 = mfma(a, f1[kk], x1);
+      const bf16x8 a2 = SHARED_K ? a : lds_a_frag<D>(lk2, col, kk, h);
+      x2 = mfma(a2, f2[kk], x2);
+    }
+    const bool full = (key0 + BT <= s.nk) && (!CAUSAL || key0 + BT - 1 <= qw0);
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float e1 = x1[r], e2 = x2[r];
+      const float d12 = e1 - e2;
+      if (!full) {
+        const int key = key0 + acc_row(r, h);
+        const bool ok = key < s.nk && (!CAUSAL || key <= query);
+        e1 = ok ? e1 : -kInf;
+        e2 = ok ? e2 : -kInf;
+      }
+      const float p1 = exp2_hw(fmaf(e1, c, b1));
+      if (SETTING == 1) {
+        ds[r] = exp2_hw(fmaf(e2, c, b2)) - p1;
+      } else {
+        ds[r] = p1 * fmaf(d12, s.scale, cst);
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const bf16x8 a = pack8(ds + 8 * cc);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dq[nb] = mfma(a, lds_bt_frag<D>(lkf, 16 * cc, nb * 32), dq[nb]);
+    }
+  }
+  __syncthreads();
+  if (!wave_live) return;
+  const long long obase = (long long)slice * s.nq;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qr = qw0 + acc_row(r, h);
+    if (qr < s.nq) {
+      const float gsc = gscale[w][acc_row(r, h)];
+      __bf16* dst = dq_out + (obase + qr) * D + col;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dst[nb * 32] = static_cast<__bf16>(dq[nb][r] * gsc);
+    }
+  }
+}
+
+// ================================================================ backward: dK (key-major)
+template <int D, int SETTING, bool CAUSAL, bool SHARED_K>
+__global__ void __launch_bounds__(kThreads)
+dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
+          const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
+          const float* __restrict__ lse1, const float* __restrict__ lse2,
+          const float* __restrict__ klv, const float* __restrict__ gv,
+          __bf16* __restrict__ dk_out, Shape s) {
+  constexpr int BKW = 32 * kWaves, BT = 32, KS = D / 16, NB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t lq1[BT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lq2[BT * D];
+  // per query of the current tile: bias of P1, bias of P2 (setting 1) or the log-ratio
+  // constant LSE2 - LSE1 - KL (setting 2), and g
+  __shared__ __attribute__((aligned(16))) float qa[3][BT];
+
+  int rank, slice;
+  block_coords(s.bh, rank, slice);
+  const int kb = rank;  // causal: small kb sees the most queries, so it runs first
+  const int b = slice / s.heads, hd = slice - b * s.heads;
+  const uint16_t* Q1 = q1 + b * s.q_sb + hd * s.q_sh;
+  const uint16_t* Q2 = q2 + b * s.q_sb + hd * s.q_sh;
+  const uint16_t* K1 = k1 + b * s.k_sb + hd * s.k_sh;
+  const uint16_t* K2 = k2 + b * s.k_sb + hd * s.k_sh;
+  const uint16_t* lqf = SETTING == 1 ? lq2 : lq1;  // free-side Q tile
+  const long long rbase = (long long)slice * s.nq;
+
+  const int l = lane_id(), w = wave_id(), h = l >> 5, col = l & 31;
+  const int kw0 = kb * BKW + w * 32;
+  const int key = kw0 + col;
+  const int krow = key < s.nk ? key : s.nk - 1;
+
+  bf16x8 f1[KS], f2[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    f1[kk] = load_frag(K1 + (long long)krow * s.k_sr + kk * 16 + h * 8);
+    f2[kk] = SHARED_K ? f1[kk] : load_frag(K2 + (long long)krow * s.k_sr + kk * 16 + h * 8);
+  }
+  const float c = s.scale * kLog2e;
+  const int t0 = CAUSAL ? (kb * BKW) / BT : 0;
+  const int t1 = (s.nq + BT - 1) / BT;
+  const bool wave_live = kw0 < s.nk;
+
+  f32x16 dk[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) dk[nb] = f32x16{};
+
+  TileRegs<BT, D> r1, r2;
+  if (t0 < t1) {
+    r1.load(Q1, s.q_sr, t0 * BT, s.nq);
+    r2.load(Q2, s.q_sr, t0 * BT, s.nq);
+  }
+  for (int t = t0; t < t1; ++t) {
+    __syncthreads();
+    r1.store(lq1);
+    r2.store(lq2);
+    if (threadIdx.x < BT) {
+      const int q = t * BT + threadIdx.x;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+      if (q < s.nq) {
+        const float x1 = lse1[rbase + q], x2 = lse2[rbase + q];
+        a0 = -x1 * kLog2e;
+        a1 = SETTING == 1 ? -x2 * kLog2e : (x2 - x1) - klv[rbase + q];
+        a2 = gv[rbase + q];
+      }
+      qa[0][threadIdx.x] = a0;
+      qa[1][threadIdx.x] = a1;
+      qa[2][threadIdx.x] = a2;
+    }
+    __syncthreads();
+    if (t + 1 < t1) {
+      r1.load(Q1, s.q_sr, (t + 1) * BT, s.nq);
+      r2.load(Q2, s.q_sr, (t + 1) * BT, s.nq);
+    }
+    const int qt0 = t * BT;
+    if (!wave_live) continue;
+    if (CAUSAL && qt0 + BT - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
+    f32x16 x1 = {}, x2 = {};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      x1 = mfma(lds_a_frag<D>(lq1, col, kk, h), f1[kk], x1);
+      x2 = mfma(lds_a_frag<D>(lq2, col, kk, h), f2[kk], x2);
+    }
+    const bool full = (qt0 + BT <= s.nq) && (!CAUSAL || qt0 >= kw0 + 31);
+    float ds[16];
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      // registers 4rq..4rq+3 hold 4 consecutive queries
+      const int qi = rq * 8 + h * 4;
+      const float4 va0 = *reinterpret_cast<const float4*>(&qa[0][qi]);
+      const float4 va1 = *reinterpret_cast<const float4*>(&qa[1][qi]);
+      const float4 va2 = *reinterpret_cast<const float4*>(&qa[2][qi]);
+      const float c0[4] = {va0.x, va0.y, va0.z, va0.w};
+      const float c1[4] = {va1.x, va1.y, va1.z, va1.w};
+      const float c2[4] = {va2.x, va2.y, va2.z, va2.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = rq * 4 + j;
+        float e1 = x1[r], e2 = x2[r];
+        const float d12 = e1 - e2;
+        if (!full) {
+          const int q = qt0 + qi + j;
+          const bool ok = q < s.nq && (!CAUSAL || key <= q);
+          e1 = ok ? e1 : -kInf;
+          e2 = ok ? e2 : -kInf;
+        }
+        const float p1 = exp2_hw(fmaf(e1, c, c0[j]));
+        if (SETTING == 1) {
+          ds[r] = c2[j] * (exp2_hw(fmaf(e2, c, c1[j])) - p1);
+        } else {
+          ds[r] = c2[j] * (p1 * fmaf(d12, s.scale, c1[j]));
+        }
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const bf16x8 a = pack8(ds + 8 * cc);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dk[nb] = mfma(a, lds_bt_frag<D>(lqf, 16 * cc, nb * 32), dk[nb]);
+    }
+  }
+  if (!wave_live) return;
+  const long long obase = (long long)slice * s.nk;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kr = kw0 + acc_row(r, h);
+    if (kr < s.nk) {
+      __bf16* dst = dk_out + (obase + kr) * D + col;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dst[nb * 32] = static_cast<__bf16>(dk[nb][r] * s.scale);
+    }
+  }
+}
+
+// ================================================================ host side
+thread_local std::string g_last_error;
+
+streamkl_status_t fail(streamkl_status_t st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Span tensor_span(const void* p, int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* st,
+                 int64_t elem) {
+  const int64_t last = (B - 1) * st[0] + (H - 1) * st[1] + (N - 1) * st[2] + D;
+  return {reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (uintptr_t)(last * elem)};
+}
+
+Span flat_span(const void* p, int64_t n, int64_t elem) {
+  return {reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (uintptr_t)(n * elem)};
+}
+
+streamkl_status_t validate(const streamkl_problem_t* p, const void* q1, const void* k1,
+                           const void* q2, const void* k2, Shape* s) {
+  if (!p) return fail(STREAMKL_ERROR_INVALID_VALUE, "problem is NULL");
+  if (p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1)
+    return fail(STREAMKL_ERROR_INVALID_VALUE, "batch, heads, n_q and n_k must be >= 1");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(STREAMKL_ERROR_NOT_SUPPORTED, "head_dim must be 64 or 128");
+  if (!(p->scale > 0.f) || !(p->scale < __builtin_huge_valf()))
+    return fail(STREAMKL_ERROR_INVALID_VALUE, "scale must be finite and > 0");
+  if (p->causal != 0 && p->causal != 1) return fail(STREAMKL_ERROR_INVALID_VALUE, "causal must be 0 or 1");
+  const int64_t lim = (int64_t)1 << 30;
+  if (p->n_q >= lim || p->n_k >= lim || p->batch * p->heads >= lim)
+    return fail(STREAMKL_ERROR_INVALID_VALUE, "sizes too large");
+  const int64_t nblk = (p->n_q > p->n_k ? p->n_q : p->n_k) / 128 + 1;
+  if (nblk * p->batch * p->heads >= ((int64_t)1 << 31))
+    return fail(STREAMKL_ERROR_INVALID_VALUE, "grid too large");
+  for (int i = 0; i < 3; ++i) {
+    if (p->q_stride[i] < 0 || p->k_stride[i] < 0 || p->q_stride[i] % 8 || p->k_stride[i] % 8)
+      return fail(STREAMKL_ERROR_INVALID_VALUE, "strides must be non-negative multiples of 8");
+  }
+  if (p->q_stride[2] < p->head_dim || p->k_stride[2] < p->head_dim)
+    return fail(STREAMKL_ERROR_INVALID_VALUE, "row stride must be >= head_dim");
+  const void* in[4] = {q1, k1, q2, k2};
+  for (const void* x : in) {
+    if (!x) return fail(STREAMKL_ERROR_INVALID_VALUE, "input pointer is NULL");
+    if (reinterpret_cast<uintptr_t>(x) % 16) return fail(STREAMKL_ERROR_INVALID_VALUE, "inputs must be 16-byte aligned");
+  }
+  s->nq = (int)p->n_q;
+  s->nk = (int)p->n_k;
+  s->bh = (int)(p->batch * p->heads);
+  s->heads = (int)p->heads;
+  s->q_sb = p->q_stride[0];
+  s->q_sh = p->q_stride[1];
+  s->q_sr = p->q_stride[2];
+  s->k_sb = p->k_stride[0];
+  s->k_sh = p->k_stride[1];
+  s->k_sr = p->k_stride[2];
+  s->scale = p->scale;
+  return STREAMKL_SUCCESS;
+}
+
+streamkl_status_t check_outputs(const streamkl_problem_t* p, const void* q1, const void* k1,
+                                const void* q2, const void* k2, const Span* outs, int n_out,
+                                const char* what) {
+  const Span in[4] = {
+      tensor_span(q1, p->batch, p->heads, p->n_q, p->head_dim, p->q_stride, 2),
+      tensor_span(k1, p->batch, p->heads, p->n_k, p->head_dim, p->k_stride, 2),
+      tensor_span(q2, p->batch, p->heads, p->n_q, p->head_dim, p->q_stride, 2),
+      tensor_span(k2, p->batch, p->heads, p->n_k, p->head_dim, p->k_stride, 2)};
+  for (int i = 0; i < n_out; ++i) {
+    if (outs[i].lo == 0) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": output pointer is NULL");
+    if (outs[i].lo % 16) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": outputs must be 16-byte aligned");
+    for (const Span& x : in)
+      if (overlaps(outs[i], x)) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": output overlaps an input");
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": outputs overlap");
+  }
+  return STREAMKL_SUCCESS;
+}
+
+streamkl_status_t check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(STREAMKL_ERROR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  g_last_error.clear();
+  return STREAMKL_SUCCESS;
+}
+
+template <int D, bool CAUSAL, bool SK>
+void launch_fwd(const Shape& s, const void* q1, const void* k1, const void* q2, const void* k2,
+                float* kl, float* l1, float* l2, hipStream_t st) {
+  const int nqb = (s.nq + 128 - 1) / 128;
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SK>), dim3(nqb * s.bh), dim3(kThreads), 0, st,
+                     (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
+                     (const uint16_t*)k2, kl, l1, l2, s);
+}
+
+template <int D, int SET, bool CAUSAL, bool SK>
+void launch_bwd(const Shape& s, const void* q1, const void* k1, const void* q2, const void* k2,
+                const float* l1, const float* l2, const float* kl, const float* g, void* dq,
+                void* dk, hipStream_t st) {
+  const int nqb = (s.nq + 128 - 1) / 128;
+  const int nkb = (s.nk + 128 - 1) / 128;
+  hipLaunchKernelGGL((dq_kernel<D, SET, CAUSAL, SK>), dim3(nqb * s.bh), dim3(kThreads), 0, st,
+                     (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
+                     (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dq, s);
+  hipLaunchKernelGGL((dk_kernel<D, SET, CAUSAL, SK>), dim3(nkb * s.bh), dim3(kThreads), 0, st,
+                     (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
+                     (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dk, s);
+}
+
+template <int SET>
+void dispatch_bwd(int64_t d, bool causal, bool sk, const Shape& s, const void* q1,
+                  const void* k1, const void* q2, const void* k2, const float* l1,
+                  const float* l2, const float* kl, const float* g, void* dq, void* dk,
+                  hipStream_t st) {
+#define SKL_BWD(DD, C, S) launch_bwd<DD, SET, C, S>(s, q1, k1, q2, k2, l1, l2, kl, g, dq, dk, st)
+  if (d == 64) {
+    if (causal) { if (sk) SKL_BWD(64, true, true); else SKL_BWD(64, true, false); }
+    else { if (sk) SKL_BWD(64, false, true); else SKL_BWD(64, false, false); }
+  } else {
+    if (causal) { if (sk) SKL_BWD(128, true, true); else SKL_BWD(128, true, false); }
+    else { if (sk) SKL_BWD(128, false, true); else SKL_BWD(128, false, false); }
+  }
+#undef SKL_BWD
+}
+
+}  // namespace
+
+extern "C" {
+
+streamkl_status_t streamkl_fwd(const streamkl_problem_t* p, const void* q1, const void* k1,
+                               const void* q2, const void* k2, float* kl, float* lse1,
+                               float* lse2, hipStream_t stream) {
+  Shape s;
+  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
+  if (st != STREAMKL_SUCCESS) return st;
+  const int64_t n = p->batch * p->heads * p->n_q;
+  const Span outs[3] = {flat_span(kl, n, 4), flat_span(lse1, n, 4), flat_span(lse2, n, 4)};
+  st = check_outputs(p, q1, k1, q2, k2, outs, 3, "streamkl_fwd");
+  if (st != STREAMKL_SUCCESS) return st;
+  (void)hipGetLastError();
+  const bool sk = k1 == k2, causal = p->causal != 0;
+#define SKL_FWD(DD, C, S) launch_fwd<DD, C, S>(s, q1, k1, q2, k2, kl, lse1, lse2, stream)
+  if (p->head_dim == 64) {
+    if (causal) { if (sk) SKL_FWD(64, true, true); else SKL_FWD(64, true, false); }
+    else { if (sk) SKL_FWD(64, false, true); else SKL_FWD(64, false, false); }
+  } else {
+    if (causal) { if (sk) SKL_FWD(128, true, true); else SKL_FWD(128, true, false); }
+    else { if (sk) SKL_FWD(128, false, true); else SKL_FWD(128, false, false); }
+  }
+#undef SKL_FWD
+  return check_launch("streamkl_fwd");
+}
+
+streamkl_status_t streamkl_bwd_fixP1(const streamkl_problem_t* p, const void* q1,
+                                     const void* k1, const void* q2, const void* k2,
+                                     const float* lse1, const float* lse2, const float* grad_kl,
+                                     void* dq2, void* dk2, hipStream_t stream) {
+  Shape s;
+  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
+  if (st != STREAMKL_SUCCESS) return st;
+  const int64_t n = p->batch * p->heads * p->n_q;
+  if (!lse1 || !lse2 || !grad_kl) return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_bwd_fixP1: NULL lse/grad pointer");
+  const Span outs[2] = {flat_span(dq2, n * p->head_dim, 2),
+                        flat_span(dk2, p->batch * p->heads * p->n_k * p->head_dim, 2)};
+  st = check_outputs(p, q1, k1, q2, k2, outs, 2, "streamkl_bwd_fixP1");
+  if (st != STREAMKL_SUCCESS) return st;
+  const Span vin[3] = {flat_span(lse1, n, 4), flat_span(lse2, n, 4), flat_span(grad_kl, n, 4)};
+  for (const Span& o : outs)
+    for (const Span& v : vin)
+      if (overlaps(o, v)) return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_bwd_fixP1: output overlaps an input");
+  (void)hipGetLastError();
+  dispatch_bwd<1>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, lse1, lse2, nullptr,
+                  grad_kl, dq2, dk2, stream);
+  return check_launch("streamkl_bwd_fixP1");
+}
+
+streamkl_status_t streamkl_bwd_fixP2(const streamkl_problem_t* p, const void* q1,
+                                     const void* k1, const void* q2, const void* k2,
+                                     const float* lse1, const float* lse2, const float* kl,
+                                     const float* grad_kl, void* dq1, void* dk1,
+                                     hipStream_t stream) {
+  Shape s;
+  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
+  if (st != STREAMKL_SUCCESS) return st;
+  const int64_t n = p->batch * p->heads * p->n_q;
+  if (!lse1 || !lse2 || !kl || !grad_kl) return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_bwd_fixP2: NULL lse/kl/grad pointer");
+  const Span outs[2] = {flat_span(dq1, n * p->head_dim, 2),
+                        flat_span(dk1, p->batch * p->heads * p->n_k * p->head_dim, 2)};
+  st = check_outputs(p, q1, k1, q2, k2, outs, 2, "streamkl_bwd_fixP2");
+  if (st != STREAMKL_SUCCESS) return st;
+  const Span vin[4] = {flat_span(lse1, n, 4), flat_span(lse2, n, 4), flat_span(kl, n, 4),
+                       flat_span(grad_kl, n, 4)};
+  for (const Span& o : outs)
+    for (const Span& v : vin)
+      if (overlaps(o, v)) return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_bwd_fixP2: output overlaps an input");
+  (void)hipGetLastError();
+  dispatch_bwd<2>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, lse1, lse2, kl,
+                  grad_kl, dq1, dk1, stream);
+  return check_launch("streamkl_bwd_fixP2");
+}
+
+const char* streamkl_status_string(streamkl_status_t status) {
+  switch (status) {
+    case STREAMKL_SUCCESS: return "STREAMKL_SUCCESS";
+    case STREAMKL_ERROR_INVALID_VALUE: return "STREAMKL_ERROR_INVALID_VALUE";
+    case STREAMKL_ERROR_NOT_SUPPORTED: return "STREAMKL_ERROR_NOT_SUPPORTED";
+    case STREAMKL_ERROR_HIP: return "STREAMKL_ERROR_HIP";
+  }
+  return "STREAMKL_UNKNOWN_STATUS";
+}
+
+const char* streamkl_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

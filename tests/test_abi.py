@@ -1,0 +1,109 @@
+"""C ABI contract, on the CPU: the library loads, exports every function the header declares,
+and rejects invalid calls with the documented status before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import online_attention_kl_amd as skl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "streamkl.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(skl.LIB_PATH),
+                                reason="libstreamkl.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(streamkl_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(skl.EXPORTS)
+    L = skl.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = skl.lib()
+    for code, name in skl.STATUS.items():
+        assert L.streamkl_status_string(code).decode() == name
+    assert L.streamkl_status_string(99).decode() == "STREAMKL_UNKNOWN_STATUS"
+
+
+def good_problem(d=128):
+    p = skl.Problem()
+    p.batch, p.heads, p.n_q, p.n_k, p.head_dim = 1, 2, 64, 80, d
+    for i, s in enumerate((2 * 64 * d, 64 * d, d)):
+        p.q_stride[i] = s
+    for i, s in enumerate((2 * 80 * d, 80 * d, d)):
+        p.k_stride[i] = s
+    p.scale = 0.125
+    p.causal = 0
+    return p
+
+
+# Fake, never-dereferenced device addresses: validation returns before any launch.
+Q1, K1, Q2, K2 = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+O1, O2, O3 = 0x50000000, 0x60000000, 0x70000000
+
+
+def fwd(p, q1=Q1, k1=K1, q2=Q2, k2=K2, o=(O1, O2, O3)):
+    return skl.lib().streamkl_fwd(ctypes.byref(p) if p is not None else None, q1, k1, q2, k2,
+                                  *o, None)
+
+
+def last_error():
+    return skl.lib().streamkl_last_error().decode()
+
+
+def test_invalid_problem_values():
+    assert fwd(None) == 1
+    p = good_problem()
+    p.n_q = 0
+    assert fwd(p) == 1 and "n_q" in last_error()
+    p = good_problem(d=96)
+    for i in range(3):
+        p.q_stride[i] = p.k_stride[i] = 96
+    assert fwd(p) == 2 and "head_dim" in last_error()
+    p = good_problem()
+    p.scale = float("nan")
+    assert fwd(p) == 1
+    p = good_problem()
+    p.scale = -1.0
+    assert fwd(p) == 1
+    p = good_problem()
+    p.causal = 2
+    assert fwd(p) == 1
+    p = good_problem()
+    p.q_stride[2] = 100
+    assert fwd(p) == 1 and "stride" in last_error()
+    p = good_problem()
+    p.k_stride[2] = 64
+    assert fwd(p) == 1
+
+
+def test_invalid_pointers():
+    p = good_problem()
+    assert fwd(p, q1=0) == 1
+    assert fwd(p, k2=K2 + 8) == 1 and "aligned" in last_error()
+    assert fwd(p, o=(O1, 0, O3)) == 1
+    assert fwd(p, o=(Q1 + 64, O2, O3)) == 1 and "overlap" in last_error()
+    assert fwd(p, o=(O1, O1 + 16, O3)) == 1
+    L = skl.lib()
+    # backward: outputs overlapping the lse / grad vectors are rejected
+    r = L.streamkl_bwd_fixP1(ctypes.byref(p), Q1, K1, Q2, K2, O1, O2, O3, O1, 0x7F000000, None)
+    assert r == 1
+    r = L.streamkl_bwd_fixP2(ctypes.byref(p), Q1, K1, Q2, K2, O1, O2, None, O3, 0x7E000000,
+                             0x7F000000, None)
+    assert r == 1
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        skl.lib(str(tmp_path / "nope.so"))

@@ -1,0 +1,153 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element by element, at
+sizes the oracle finishes in seconds that still span several tiles and ragged tails."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import online_attention_kl_amd as skl
+import oracle
+from parity_util import assert_grad_close, assert_rows_close, dev_bf16, f64, grad_atol, to_np
+from workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+# (batch, heads, n_q, n_k, head_dim, causal)
+SHAPES = [
+    (1, 1, 1, 1, 64, False),
+    (1, 1, 1, 1, 128, True),
+    (1, 2, 17, 33, 64, False),
+    (1, 1, 64, 64, 128, True),
+    (2, 1, 65, 65, 64, True),
+    (1, 1, 255, 257, 128, False),
+    (1, 2, 257, 255, 128, True),
+    (1, 1, 1000, 1000, 64, True),
+    (1, 1, 300, 700, 128, True),
+    (1, 1, 700, 300, 64, True),
+    (1, 1, 129, 1024, 128, False),
+    (1, 3, 384, 384, 128, False),
+]
+
+
+def shape_id(s):
+    return "B{}H{}_q{}_k{}_d{}_{}".format(*s[:5], "causal" if s[5] else "full")
+
+
+def make(shape, recipe="iid", seed=123, g_mode="uniform"):
+    B, H, nq, nk, d, causal = shape
+    w = Workload("test", B, H, nq, nk, d, causal, (1, 2), seed, recipe, sigma=0.3,
+                 g_mode=g_mode)
+    x = make_inputs(w)
+    dev = {n: dev_bf16(x[n]) for n in ("q1", "k1", "q2")}
+    dev["k2"] = dev["k1"] if x["k2"] is x["k1"] else dev_bf16(x["k2"])
+    dev["g"] = torch.from_numpy(x["g"]).cuda()
+    ref = {n: f64(x[n]) for n in ("q1", "k1", "q2", "k2")}
+    ref["g"] = x["g"].astype(np.float64)
+    return w, dev, ref
+
+
+def check_grads(w, r, setting, dq, dk, rdq, rdk, lse_max, tag=""):
+    qf, kf = (r["q2"], r["k2"]) if setting == 1 else (r["q1"], r["k1"])
+    aq = grad_atol(w.scale, r["g"], lse_max, kf)
+    ak = grad_atol(w.scale, r["g"], lse_max, qf, mass=w.n_q / w.n_k)
+    assert_grad_close(to_np(dq), rdq, f"{tag}setting {setting} dQ", aq)
+    assert_grad_close(to_np(dk), rdk, f"{tag}setting {setting} dK", ak)
+
+
+def announce(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=shape_id)
+@pytest.mark.parametrize("recipe", ["iid", "perturb", "shared_k"])
+def test_forward_and_backward(shape, recipe):
+    announce(f"parity {shape_id(shape)} {recipe}")
+    w, d, r = make(shape, recipe)
+    kl, l1, l2 = skl.streamkl_fwd(d["q1"], d["k1"], d["q2"], d["k2"], causal=w.causal)
+    rk, r1, r2 = oracle.forward(r["q1"], r["k1"], r["q2"], r["k2"], w.scale, w.causal)
+    assert_rows_close(to_np(kl), rk, "KL")
+    assert_rows_close(to_np(l1), r1, "LSE1")
+    assert_rows_close(to_np(l2), r2, "LSE2")
+    for setting in (1, 2):
+        if setting == 1:
+            dq, dk = skl.streamkl_bwd_fixP1(d["q1"], d["k1"], d["q2"], d["k2"], l1, l2, d["g"],
+                                            causal=w.causal)
+        else:
+            dq, dk = skl.streamkl_bwd_fixP2(d["q1"], d["k1"], d["q2"], d["k2"], l1, l2, kl,
+                                            d["g"], causal=w.causal)
+        rdq, rdk = oracle.backward(setting, r["q1"], r["k1"], r["q2"], r["k2"], r["g"], w.scale,
+                                   w.causal)
+        check_grads(w, r, setting, dq, dk, rdq, rdk, max(np.abs(r1).max(), np.abs(r2).max()))
+
+
+@pytest.mark.parametrize("shape", [SHAPES[5], SHAPES[7]], ids=shape_id)
+def test_backward_from_oracle_state(shape):
+    """The backward fed with the oracle's own LSE / KL (rounded to fp32), isolating it from
+    forward error."""
+    announce(f"bwd-from-oracle {shape_id(shape)}")
+    w, d, r = make(shape, "perturb")
+    rk, r1, r2 = oracle.forward(r["q1"], r["k1"], r["q2"], r["k2"], w.scale, w.causal)
+    t = [torch.from_numpy(a.astype(np.float32)).cuda() for a in (rk, r1, r2)]
+    dq, dk = skl.streamkl_bwd_fixP1(d["q1"], d["k1"], d["q2"], d["k2"], t[1], t[2], d["g"],
+                                    causal=w.causal)
+    lmax = max(np.abs(r1).max(), np.abs(r2).max())
+    rdq, rdk = oracle.backward(1, r["q1"], r["k1"], r["q2"], r["k2"], r["g"], w.scale, w.causal)
+    check_grads(w, r, 1, dq, dk, rdq, rdk, lmax)
+    dq, dk = skl.streamkl_bwd_fixP2(d["q1"], d["k1"], d["q2"], d["k2"], t[1], t[2], t[0], d["g"],
+                                    causal=w.causal)
+    rdq, rdk = oracle.backward(2, r["q1"], r["k1"], r["q2"], r["k2"], r["g"], w.scale, w.causal)
+    check_grads(w, r, 2, dq, dk, rdq, rdk, lmax)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_inputs_give_exact_zeros(causal):
+    announce(f"identical causal={causal}")
+    w, d, r = make((1, 2, 300, 300, 128, causal))
+    kl, l1, l2 = skl.streamkl_fwd(d["q1"], d["k1"], d["q1"], d["k1"], causal=causal)
+    assert torch.all(kl == 0) and torch.equal(l1, l2)
+    dq, dk = skl.streamkl_bwd_fixP1(d["q1"], d["k1"], d["q1"], d["k1"], l1, l2, d["g"],
+                                    causal=causal)
+    assert torch.all(dq == 0) and torch.all(dk == 0)
+    dq, dk = skl.streamkl_bwd_fixP2(d["q1"], d["k1"], d["q1"], d["k1"], l1, l2, kl, d["g"],
+                                    causal=causal)
+    assert torch.all(dq == 0) and torch.all(dk == 0)
+
+
+def test_forward_is_deterministic():
+    announce("determinism")
+    w, d, r = make((1, 4, 1000, 1000, 128, True), "perturb")
+    a = skl.streamkl_fwd(d["q1"], d["k1"], d["q2"], d["k2"], causal=True)
+    for _ in range(3):
+        b = skl.streamkl_fwd(d["q1"], d["k1"], d["q2"], d["k2"], causal=True)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+    g1 = skl.streamkl_bwd_fixP1(d["q1"], d["k1"], d["q2"], d["k2"], a[1], a[2], d["g"], causal=True)
+    g2 = skl.streamkl_bwd_fixP1(d["q1"], d["k1"], d["q2"], d["k2"], a[1], a[2], d["g"], causal=True)
+    assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1])
+
+
+def test_strided_inputs():
+    """[B, N, H, d] storage viewed as [B, H, N, d]: strides (N*H*d, d, H*d)."""
+    announce("strided")
+    B, H, nq, nk, dd = 2, 3, 200, 150, 64
+    w, d, r = make((B, H, nq, nk, dd, True), "perturb")
+    sd = {n: d[n].transpose(1, 2).contiguous().transpose(1, 2) for n in ("q1", "k1", "q2", "k2")}
+    assert sd["q1"].stride() == (nq * H * dd, dd, H * dd, 1)
+    kl, l1, l2 = skl.streamkl_fwd(sd["q1"], sd["k1"], sd["q2"], sd["k2"], causal=True)
+    rk, r1, r2 = oracle.forward(r["q1"], r["k1"], r["q2"], r["k2"], w.scale, True)
+    assert_rows_close(to_np(kl), rk, "KL")
+    dq, dk = skl.streamkl_bwd_fixP1(sd["q1"], sd["k1"], sd["q2"], sd["k2"], l1, l2, d["g"],
+                                    causal=True)
+    rdq, rdk = oracle.backward(1, r["q1"], r["k1"], r["q2"], r["k2"], r["g"], w.scale, True)
+    check_grads(w, r, 1, dq, dk, rdq, rdk, max(np.abs(r1).max(), np.abs(r2).max()))
+
+
+def test_invalid_call_raises():
+    announce("invalid")
+    w, d, r = make((1, 1, 64, 64, 64, False))
+    bad = torch.empty((1, 1, 64, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(skl.StreamKLError) as e:
+        skl.streamkl_fwd(bad, bad, bad, bad)
+    assert e.value.status == 2

@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""StreamKL benchmark on one MI355X: forward + backward over one batch of synthetic input.
+
+A step is one pass of the whole hot path: the forward (per-row KL, LSE1, LSE2) followed by the
+backward of every setting the workload names (dQ kernel, then dK kernel). Inputs are generated
+on the host from the seeded generator, copied to HBM once, and stay resident; the timed region
+covers exactly `--steps` steps between two device synchronisations. Each kernel is bracketed
+by HIP events on the stream it is launched on, which gives the per-launch durations used for
+the roofline of the dominant kernel.
+
+Algorithmic work per visible (query, key) pair: forward 4 d flop (two QK^T contractions),
+backward 8 d flop per setting (two recomputed contractions and the dQ and dK products). The
+two backward kernels are each credited with half of the backward's 8 d (the dQ kernel's
+recomputation of S repeats work the dK kernel also does, and is not counted twice).
+
+Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import WORKLOADS, bf16_bits_to_f32, make_inputs, visible_pairs  # noqa: E402
+
+METRIC = "StreamKL fwd+bwd TFLOP/s and % bf16 MFMA peak, H=32 N=64K d=128 causal"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+KERNEL_SOURCE = os.path.join(ROOT, "online_attention_kl_amd", "csrc", "streamkl_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when the kernel
+    source has changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_sha() or t.get("workload") != workload:
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
+
+
+def cpu_baseline(w, x, target_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload: blocks of 256
+    query rows spread evenly over the row range of several slices, forward plus the workload's
+    backward settings restricted to those rows, one slice's rows per worker thread."""
+    import numpy as np
+    from oracle.reference import backward_slice, default_workers, forward_slice, pool_map
+
+    workers = min(default_workers(), w.batch * w.heads)
+    nblk = max(1, w.n_q // 256)
+    slices = [(i // w.heads, i % w.heads) for i in range(workers)]
+    f64 = {}
+    for (b, h) in slices:
+        f64[(b, h)] = {n: bf16_bits_to_f32(x[n][b, h]).reshape(x[n][b, h].shape).astype(np.float64)
+                       for n in ("q1", "k1", "q2", "k2")}
+
+    def rows_pairs(rows):
+        if w.causal:
+            return int(np.minimum(rows + 1, w.n_k).sum())
+        return rows.shape[0] * w.n_k
+
+    def run(item):
+        (b, h), blk = item
+        r0 = min(blk * 256, w.n_q - 1)
+        rows = np.arange(r0, min(r0 + 256, w.n_q))
+        a = f64[(b, h)]
+        forward_slice(a["q1"], a["k1"], a["q2"], a["k2"], w.scale, w.causal, rows=rows)
+        for s in w.settings:
+            backward_slice(s, a["q1"], a["k1"], a["q2"], a["k2"], x["g"][b, h], w.scale, w.causal,
+                           rows=rows)
+        return rows_pairs(rows)
+
+    # calibrate: one round (one block per worker) tells how many rounds fit the target time
+    def blocks_for(round_idx, rounds):
+        # spread the sampled blocks evenly over the row range
+        return [int((round_idx + 0.5) * nblk / rounds) for _ in range(workers)]
+
+    t0 = time.perf_counter()
+    pairs = sum(pool_map(run, list(zip(slices, blocks_for(0, 2))), workers))
+    first = time.perf_counter() - t0
+    rounds = max(1, min(64, int(target_s / max(first, 1e-3))))
+    t0 = time.perf_counter()
+    pairs = 0
+    for r in range(rounds):
+        pairs += sum(pool_map(run, list(zip(slices, blocks_for(r, rounds))), workers))
+    secs = time.perf_counter() - t0
+    flop = pairs * w.head_dim * (4 + 8 * len(w.settings))
+    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "seconds": round(secs, 2),
+            "sample": f"{rounds} rounds x {workers} slices x 256 query rows (row blocks spread "
+                      f"over the range), forward + backward setting(s) {list(w.settings)} "
+                      f"restricted to those rows, fp64 numpy, {pairs} visible pairs"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="causal_64k_d128", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the StreamKL path here runs on a single MI355X "
+              "(slices would shard across GPUs with no communication; not built). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    w = WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = make_inputs(w)
+
+    import numpy as np
+    import torch
+    import online_attention_kl_amd as skl
+
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q1, q2 = up(x["q1"]), up(x["q2"])
+    k1 = up(x["k1"])
+    k2 = k1 if x["k2"] is x["k1"] else up(x["k2"])
+    g = torch.from_numpy(x["g"]).to(dev)
+    B, H, nq, nk, d = w.batch, w.heads, w.n_q, w.n_k, w.head_dim
+    f32 = dict(dtype=torch.float32, device=dev)
+    kl, l1, l2 = (torch.empty((B, H, nq), **f32) for _ in range(3))
+    grads = {s: (torch.empty(q1.shape, dtype=torch.bfloat16, device=dev),
+                 torch.empty(k1.shape, dtype=torch.bfloat16, device=dev)) for s in w.settings}
+    base_bytes = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+
+    names = ["fwd_kernel"] + [f"{k}_kernel_s{s}" for s in w.settings for k in ("dq", "dk")]
+
+    def step(ev=None):
+        i = 0
+
+        def mark():
+            nonlocal i
+            if ev is not None:
+                ev[i].record()
+            i += 1
+        mark()
+        skl.streamkl_fwd(q1, k1, q2, k2, causal=w.causal, out=(kl, l1, l2))
+        mark()
+        for s in w.settings:
+            skl.streamkl_bwd_dq(s, q1, k1, q2, k2, l1, l2, kl, g, causal=w.causal, out=grads[s][0])
+            mark()
+            skl.streamkl_bwd_dk(s, q1, k1, q2, k2, l1, l2, kl, g, causal=w.causal, out=grads[s][1])
+            mark()
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base_bytes
+
+    pairs = visible_pairs(w)
+    fwd_flop = 4 * d * pairs
+    bwd_flop = 8 * d * pairs
+    step_flop = fwd_flop + bwd_flop * len(w.settings)
+    value = step_flop / (ms_step * 1e-3) / 1e12
+    alg = {"fwd_kernel": fwd_flop}
+    for s in w.settings:
+        alg[f"dq_kernel_s{s}"] = bwd_flop / 2
+        alg[f"dk_kernel_s{s}"] = bwd_flop / 2
+    dom = max(kms, key=kms.get)
+    achieved = alg[dom] / (kms[dom] * 1e-3) / 1e12
+    fwd_ms = kms["fwd_kernel"]
+    bwd_ms = sum(v for n, v in kms.items() if n != "fwd_kernel")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": B, "heads": H, "n_q": nq, "n_k": nk, "head_dim": d,
+            "causal": w.causal, "backward_settings": list(w.settings),
+            "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+            "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+            "fwd_tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(bwd_flop * len(w.settings) / (bwd_ms * 1e-3) / 1e12, 2),
+            "kernel_ms": {n: round(v, 3) for n, v in kms.items()},
+            "visible_pairs": pairs,
+            "saved_state_bytes": 3 * B * H * nq * 4,
+            "peak_extra_hbm_bytes_during_step": int(peak_extra),
+            "materialised_p1_p2_bf16_bytes_avoided": 2 * B * H * nq * nk * 2,
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for(dom, w.name),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on a host sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

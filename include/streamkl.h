@@ -110,6 +110,26 @@ streamkl_status_t streamkl_bwd_fixP2(const streamkl_problem_t* problem,
                                      const float* kl, const float* grad_kl, void* dq1, void* dk1,
                                      hipStream_t stream);
 
+/*
+ * The two halves of a backward call, one kernel each, for callers that need only one gradient
+ * (for example when K is frozen and only dQ is wanted) or that time the kernels separately.
+ * streamkl_bwd_fixP1 = streamkl_bwd_dq + streamkl_bwd_dk with setting = 1, and
+ * streamkl_bwd_fixP2 the same with setting = 2 (gist.science/pt "Metodologia" section 2:
+ * dQ accumulates along K, dK along Q; here each runs in its own kernel and neither needs
+ * atomics).
+ * setting: 1 (P1 fixed; writes dq2 / dk2) or 2 (P2 fixed; writes dq1 / dk1). kl is read only for
+ * setting 2 and may be NULL for setting 1. Other arguments as in streamkl_bwd_fixP1 / _fixP2;
+ * dq (or dk) is the one output, contiguous bfloat16 [batch, heads, n_q (or n_k), head_dim].
+ */
+streamkl_status_t streamkl_bwd_dq(const streamkl_problem_t* problem, int32_t setting,
+                                  const void* q1, const void* k1, const void* q2, const void* k2,
+                                  const float* lse1, const float* lse2, const float* kl,
+                                  const float* grad_kl, void* dq, hipStream_t stream);
+streamkl_status_t streamkl_bwd_dk(const streamkl_problem_t* problem, int32_t setting,
+                                  const void* q1, const void* k1, const void* q2, const void* k2,
+                                  const float* lse1, const float* lse2, const float* kl,
+                                  const float* grad_kl, void* dk, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* streamkl_status_string(streamkl_status_t status);
 

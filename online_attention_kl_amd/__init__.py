@@ -9,6 +9,8 @@ Functions (names follow the C ABI):
   streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False)           -> (kl, lse1, lse2)
   streamkl_bwd_fixP1(q1, k1, q2, k2, lse1, lse2, grad_kl, ...)      -> (dq2, dk2)
   streamkl_bwd_fixP2(q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...)  -> (dq1, dk1)
+  streamkl_bwd_dq(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...) -> dq (one kernel)
+  streamkl_bwd_dk(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...) -> dk (one kernel)
 Inputs are bfloat16 CUDA tensors [B, H, N, d] (the d axis contiguous, any other strides that
 are multiples of 8 elements); kl / lse / grad_kl are float32 [B, H, N_Q].
 """
@@ -23,8 +25,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamkl
 STATUS = {0: "STREAMKL_SUCCESS", 1: "STREAMKL_ERROR_INVALID_VALUE",
           2: "STREAMKL_ERROR_NOT_SUPPORTED", 3: "STREAMKL_ERROR_HIP"}
 
-EXPORTS = ("streamkl_fwd", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2",
-           "streamkl_status_string", "streamkl_last_error")
+EXPORTS = ("streamkl_fwd", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2", "streamkl_bwd_dq",
+           "streamkl_bwd_dk", "streamkl_status_string", "streamkl_last_error")
 
 
 class StreamKLError(RuntimeError):
@@ -58,7 +60,10 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.streamkl_fwd.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp]
     L.streamkl_bwd_fixP1.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp, vp, vp]
     L.streamkl_bwd_fixP2.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, fp, vp, vp, vp]
-    for name in ("streamkl_fwd", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2"):
+    for name in ("streamkl_bwd_dq", "streamkl_bwd_dk"):
+        getattr(L, name).argtypes = [pp, ctypes.c_int32, vp, vp, vp, vp, fp, fp, fp, fp, vp, vp]
+    for name in ("streamkl_fwd", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2", "streamkl_bwd_dq",
+                 "streamkl_bwd_dk"):
         getattr(L, name).restype = ctypes.c_int
     L.streamkl_status_string.argtypes = [ctypes.c_int]
     L.streamkl_status_string.restype = ctypes.c_char_p
@@ -172,3 +177,37 @@ def streamkl_bwd_fixP2(q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=None, caus
                                     kl.data_ptr(), grad_kl.data_ptr(), out[0].data_ptr(),
                                     out[1].data_ptr(), _stream(q1)))
     return out
+
+
+def _bwd_one(which, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale, causal, out):
+    import torch
+    _check_inputs(q1, k1, q2, k2)
+    B, H, nq, _ = q1.shape
+    vecs = [("lse1", lse1), ("lse2", lse2), ("grad_kl", grad_kl)]
+    if setting == 2:
+        vecs.append(("kl", kl))
+    for n, t in vecs:
+        _rowvec(t, n, (B, H, nq))
+    ref = (q2 if setting == 1 else q1) if which == "dq" else (k2 if setting == 1 else k1)
+    if out is None:
+        out = torch.empty(ref.shape, dtype=torch.bfloat16, device=ref.device)
+    if out.dtype != torch.bfloat16 or out.shape != ref.shape or not out.is_contiguous():
+        raise ValueError(f"{which} must be a contiguous bfloat16 tensor of shape {tuple(ref.shape)}")
+    p = make_problem(q1, k1, scale, causal)
+    fn = lib().streamkl_bwd_dq if which == "dq" else lib().streamkl_bwd_dk
+    _check(fn(ctypes.byref(p), setting, q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(),
+              lse1.data_ptr(), lse2.data_ptr(), kl.data_ptr() if kl is not None else None,
+              grad_kl.data_ptr(), out.data_ptr(), _stream(q1)))
+    return out
+
+
+def streamkl_bwd_dq(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=None, causal=False,
+                    out=None):
+    """dQ of the free side only (one kernel): dq2 for setting 1, dq1 for setting 2."""
+    return _bwd_one("dq", setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale, causal, out)
+
+
+def streamkl_bwd_dk(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=None, causal=False,
+                    out=None):
+    """dK of the free side only (one kernel): dk2 for setting 1, dk1 for setting 2."""
+    return _bwd_one("dk", setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale, causal, out)

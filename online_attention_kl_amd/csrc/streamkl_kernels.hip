@@ -667,12 +667,14 @@ void launch_bwd(const Shape& s, const void* q1, const void* k1, const void* q2, 
                 void* dk, hipStream_t st) {
   const int nqb = (s.nq + 128 - 1) / 128;
   const int nkb = (s.nk + 128 - 1) / 128;
-  hipLaunchKernelGGL((dq_kernel<D, SET, CAUSAL, SK>), dim3(nqb * s.bh), dim3(kThreads), 0, st,
-                     (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
-                     (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dq, s);
-  hipLaunchKernelGGL((dk_kernel<D, SET, CAUSAL, SK>), dim3(nkb * s.bh), dim3(kThreads), 0, st,
-                     (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
-                     (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dk, s);
+  if (dq)
+    hipLaunchKernelGGL((dq_kernel<D, SET, CAUSAL, SK>), dim3(nqb * s.bh), dim3(kThreads), 0, st,
+                       (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
+                       (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dq, s);
+  if (dk)
+    hipLaunchKernelGGL((dk_kernel<D, SET, CAUSAL, SK>), dim3(nkb * s.bh), dim3(kThreads), 0, st,
+                       (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
+                       (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dk, s);
 }
 
 template <int SET>
@@ -689,6 +691,41 @@ void dispatch_bwd(int64_t d, bool causal, bool sk, const Shape& s, const void* q
     else { if (sk) SKL_BWD(128, false, true); else SKL_BWD(128, false, false); }
   }
 #undef SKL_BWD
+}
+
+streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const void* q1,
+                             const void* k1, const void* q2, const void* k2, const float* lse1,
+                             const float* lse2, const float* kl, const float* grad_kl, void* dq,
+                             void* dk, bool want_dq, bool want_dk, hipStream_t stream,
+                             const char* what) {
+  Shape s;
+  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
+  if (st != STREAMKL_SUCCESS) return st;
+  if (setting != 1 && setting != 2) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": setting must be 1 or 2");
+  if (!lse1 || !lse2 || !grad_kl || (setting == 2 && !kl))
+    return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": NULL lse / kl / grad pointer");
+  const int64_t n = p->batch * p->heads * p->n_q;
+  Span outs[2];
+  int n_out = 0;
+  if (want_dq) outs[n_out++] = flat_span(dq, n * p->head_dim, 2);
+  if (want_dk) outs[n_out++] = flat_span(dk, p->batch * p->heads * p->n_k * p->head_dim, 2);
+  st = check_outputs(p, q1, k1, q2, k2, outs, n_out, what);
+  if (st != STREAMKL_SUCCESS) return st;
+  const Span vin[4] = {flat_span(lse1, n, 4), flat_span(lse2, n, 4), flat_span(grad_kl, n, 4),
+                       flat_span(setting == 2 ? kl : lse1, n, 4)};
+  for (int i = 0; i < n_out; ++i)
+    for (const Span& v : vin)
+      if (overlaps(outs[i], v)) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": output overlaps an input");
+  (void)hipGetLastError();
+  void* dqp = want_dq ? dq : nullptr;
+  void* dkp = want_dk ? dk : nullptr;
+  if (setting == 1)
+    dispatch_bwd<1>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, lse1, lse2, nullptr,
+                    grad_kl, dqp, dkp, stream);
+  else
+    dispatch_bwd<2>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, lse1, lse2, kl,
+                    grad_kl, dqp, dkp, stream);
+  return check_launch(what);
 }
 
 }  // namespace
@@ -723,23 +760,8 @@ streamkl_status_t streamkl_bwd_fixP1(const streamkl_problem_t* p, const void* q1
                                      const void* k1, const void* q2, const void* k2,
                                      const float* lse1, const float* lse2, const float* grad_kl,
                                      void* dq2, void* dk2, hipStream_t stream) {
-  Shape s;
-  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
-  if (st != STREAMKL_SUCCESS) return st;
-  const int64_t n = p->batch * p->heads * p->n_q;
-  if (!lse1 || !lse2 || !grad_kl) return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_bwd_fixP1: NULL lse/grad pointer");
-  const Span outs[2] = {flat_span(dq2, n * p->head_dim, 2),
-                        flat_span(dk2, p->batch * p->heads * p->n_k * p->head_dim, 2)};
-  st = check_outputs(p, q1, k1, q2, k2, outs, 2, "streamkl_bwd_fixP1");
-  if (st != STREAMKL_SUCCESS) return st;
-  const Span vin[3] = {flat_span(lse1, n, 4), flat_span(lse2, n, 4), flat_span(grad_kl, n, 4)};
-  for (const Span& o : outs)
-    for (const Span& v : vin)
-      if (overlaps(o, v)) return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_bwd_fixP1: output overlaps an input");
-  (void)hipGetLastError();
-  dispatch_bwd<1>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, lse1, lse2, nullptr,
-                  grad_kl, dq2, dk2, stream);
-  return check_launch("streamkl_bwd_fixP1");
+  return bwd_common(p, 1, q1, k1, q2, k2, lse1, lse2, nullptr, grad_kl, dq2, dk2, true, true,
+                    stream, "streamkl_bwd_fixP1");
 }
 
 streamkl_status_t streamkl_bwd_fixP2(const streamkl_problem_t* p, const void* q1,
@@ -747,24 +769,24 @@ streamkl_status_t streamkl_bwd_fixP2(const streamkl_problem_t* p, const void* q1
                                      const float* lse1, const float* lse2, const float* kl,
                                      const float* grad_kl, void* dq1, void* dk1,
                                      hipStream_t stream) {
-  Shape s;
-  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
-  if (st != STREAMKL_SUCCESS) return st;
-  const int64_t n = p->batch * p->heads * p->n_q;
-  if (!lse1 || !lse2 || !kl || !grad_kl) return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_bwd_fixP2: NULL lse/kl/grad pointer");
-  const Span outs[2] = {flat_span(dq1, n * p->head_dim, 2),
-                        flat_span(dk1, p->batch * p->heads * p->n_k * p->head_dim, 2)};
-  st = check_outputs(p, q1, k1, q2, k2, outs, 2, "streamkl_bwd_fixP2");
-  if (st != STREAMKL_SUCCESS) return st;
-  const Span vin[4] = {flat_span(lse1, n, 4), flat_span(lse2, n, 4), flat_span(kl, n, 4),
-                       flat_span(grad_kl, n, 4)};
-  for (const Span& o : outs)
-    for (const Span& v : vin)
-      if (overlaps(o, v)) return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_bwd_fixP2: output overlaps an input");
-  (void)hipGetLastError();
-  dispatch_bwd<2>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, lse1, lse2, kl,
-                  grad_kl, dq1, dk1, stream);
-  return check_launch("streamkl_bwd_fixP2");
+  return bwd_common(p, 2, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, dq1, dk1, true, true, stream,
+                    "streamkl_bwd_fixP2");
+}
+
+streamkl_status_t streamkl_bwd_dq(const streamkl_problem_t* p, int32_t setting, const void* q1,
+                                  const void* k1, const void* q2, const void* k2,
+                                  const float* lse1, const float* lse2, const float* kl,
+                                  const float* grad_kl, void* dq, hipStream_t stream) {
+  return bwd_common(p, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, dq, nullptr, true, false,
+                    stream, "streamkl_bwd_dq");
+}
+
+streamkl_status_t streamkl_bwd_dk(const streamkl_problem_t* p, int32_t setting, const void* q1,
+                                  const void* k1, const void* q2, const void* k2,
+                                  const float* lse1, const float* lse2, const float* kl,
+                                  const float* grad_kl, void* dk, hipStream_t stream) {
+  return bwd_common(p, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, nullptr, dk, false, true,
+                    stream, "streamkl_bwd_dk");
 }
 
 const char* streamkl_status_string(streamkl_status_t status) {

@@ -174,7 +174,8 @@ def dk_rows_slice(setting: int, q1, k1, q2, k2, g, scale: float, causal: bool, k
 
 
 # ---------------------------------------------------------------- whole tensors
-def _pool_map(fn, items, workers: int):
+def pool_map(fn, items, workers: int):
+    """Map fn over items in a thread pool of `workers` threads, BLAS limited to one thread each."""
     if workers <= 1 or len(items) <= 1:
         return [fn(x) for x in items]
     try:
@@ -198,7 +199,7 @@ def forward(q1, k1, q2, k2, scale: float, causal: bool, workers: int = 1):
     """KL, LSE1, LSE2 float64 [B, H, N_Q] for [B, H, N, d] inputs (slices in a thread pool)."""
     B, H = q1.shape[:2]
     items = [(b, h) for b in range(B) for h in range(H)]
-    res = _pool_map(lambda bh: forward_slice(q1[bh], k1[bh], q2[bh], k2[bh], scale, causal),
+    res = pool_map(lambda bh: forward_slice(q1[bh], k1[bh], q2[bh], k2[bh], scale, causal),
                     items, workers)
     out = np.empty((3, B, H, q1.shape[2]))
     for (b, h), (kl, l1, l2) in zip(items, res):
@@ -210,7 +211,7 @@ def backward(setting: int, q1, k1, q2, k2, g, scale: float, causal: bool, worker
     """(dQ_free, dK_free) float64 [B, H, N, d] for [B, H, N, d] inputs."""
     B, H = q1.shape[:2]
     items = [(b, h) for b in range(B) for h in range(H)]
-    res = _pool_map(lambda bh: backward_slice(setting, q1[bh], k1[bh], q2[bh], k2[bh], g[bh],
+    res = pool_map(lambda bh: backward_slice(setting, q1[bh], k1[bh], q2[bh], k2[bh], g[bh],
                                               scale, causal), items, workers)
     dq = np.empty(q1.shape)
     dk = np.empty(k1.shape)

@@ -91,19 +91,18 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
 }
 
 // ---------------------------------------------------------------- LDS tiles
-// A tile of ROWS rows x D bf16 values, stored as 16-byte chunks; chunk c of row r lives at
-// chunk slot r * CPR + (c ^ (r % CPR)).
+// A tile of ROWS rows x D bf16 values is stored row-major with a pitch of D + 8 elements: the
+// 16-byte pad shifts consecutive rows by four banks, so the 16 rows that one pass of a 16-byte
+// operand read touches fall in distinct banks, and every operand address of a lane is one base
+// register plus a compile-time offset.
 template <int D>
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  constexpr int CPR = D / 8;
-  return (row * CPR + (chunk ^ (row & (CPR - 1)))) * 8;
-}
+constexpr int lds_pitch() { return D + 8; }
 
-template <int ROWS, int D>
+template <int ROWS, int D, int NT>
 struct TileRegs {
   static constexpr int CPR = D / 8;
-  static constexpr int N = ROWS * CPR / kThreads;
-  static_assert(N * kThreads == ROWS * CPR, "tile must split evenly over the block");
+  static constexpr int N = ROWS * CPR / NT;
+  static_assert(N * NT == ROWS * CPR, "tile must split evenly over the block");
   uint4 v[N];
 
   // Rows row0.. of a [n_valid, D] matrix with row stride rstride; rows >= n_valid read as 0.
@@ -111,7 +110,7 @@ struct TileRegs {
                                        int row0, int n_valid) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int idx = threadIdx.x + i * kThreads;
+      const int idx = threadIdx.x + i * NT;
       const int row = idx / CPR, c = idx % CPR;
       const int gr = row0 + row;
       if (gr < n_valid)
@@ -123,9 +122,9 @@ struct TileRegs {
   __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int idx = threadIdx.x + i * kThreads;
+      const int idx = threadIdx.x + i * NT;
       const int row = idx / CPR, c = idx % CPR;
-      *reinterpret_cast<uint4*>(lds + lds_off<D>(row, c)) = v[i];
+      *reinterpret_cast<uint4*>(lds + row * lds_pitch<D>() + c * 8) = v[i];
     }
   }
 };
@@ -134,30 +133,7 @@ struct TileRegs {
 // kk * 16 + h * 8 .. +8.
 template <int D>
 __device__ __forceinline__ bf16x8 lds_a_frag(const uint16_t* lds, int row, int kk, int h) {
-  return load_frag(lds + lds_off<D>(row, kk * 2 + h));
-}
-
-// B operand [k = tile row, n = column] of a 32x32x16 MFMA read from a row-major LDS tile with
-// ds_read_b64_tr_b16. Lane l receives column colbase + (l & 31) and the 8 tile rows
-//   rowbase + (t / 4) * 8 + (l / 32) * 4 + (t % 4),  t = 0..7,
-// which is the order in which a 32x32 accumulator holds its rows (acc_row), so that an
-// accumulator's registers 8c..8c+7 form the matching A operand for rowbase = 16 c.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_bt_frag(const uint16_t* lds, int rowbase, int colbase) {
-  const int l = lane_id(), g = l >> 4, i = l & 15;
-  const int col = colbase + (g & 1) * 16 + 4 * (i & 3);
-  const int chunk = col >> 3, within = col & 7;
-  const lds_u16* base = (const lds_u16*)(lds);
-  s16x4 v[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = rowbase + 8 * j + (g >> 1) * 4 + (i >> 2);
-    const int off = lds_off<D>(row, chunk) + within;
-    v[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
-  }
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  s16x8 w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
-  return __builtin_bit_cast(bf16x8, w);
+  return load_frag(lds + row * lds_pitch<D>() + kk * 16 + h * 8);
 }
 
 // ---------------------------------------------------------------- block -> tile mapping
@@ -170,61 +146,67 @@ __device__ __forceinline__ void block_coords(int n_slices, int& rank, int& slice
 }
 
 // ================================================================ forward
-template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void fwd_tile_update(const f32x16 (&s1)[2], const f32x16 (&s2)[2],
-                                                float c, int key0, int query, int nk, int h,
-                                                float& m1, float& l1, float& m2, float& l2,
-                                                float& acc) {
-  float e1[32], e2[32], d12[32];
+// One key tile's contribution to a lane's partial online state. s1 / s2 hold the lane's 32
+// unscaled dot products of the tile (two 32-key blocks x 16 keys) and are masked in place.
+template <bool CAUSAL, bool MASK>
+__device__ __forceinline__ void fwd_tile_update(f32x16 (&s1)[2], f32x16 (&s2)[2], float c,
+                                                int key0, int query, int nk, int h, float& m1,
+                                                float& l1, float& m2, float& l2, float& acc) {
+  if (MASK) {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = rb * 16 + r;
-      e1[i] = s1[rb][r];
-      e2[i] = s2[rb][r];
-      d12[i] = e1[i] - e2[i];
-      if (MASK) {
+      for (int r = 0; r < 16; ++r) {
         const int key = key0 + rb * 32 + acc_row(r, h);
         const bool ok = key < nk && (!CAUSAL || key <= query);
-        e1[i] = ok ? e1[i] : -kInf;
-        e2[i] = ok ? e2[i] : -kInf;
+        s1[rb][r] = ok ? s1[rb][r] : -kInf;
+        s2[rb][r] = ok ? s2[rb][r] : -kInf;
       }
-    }
-  float mx1 = e1[0], mx2 = e2[0];
+  }
+  float mx1 = fmaxf(s1[0][0], s1[1][0]), mx2 = fmaxf(s2[0][0], s2[1][0]);
 #pragma unroll
-  for (int i = 1; i < 32; ++i) {
-    mx1 = fmaxf(mx1, e1[i]);
-    mx2 = fmaxf(mx2, e2[i]);
+  for (int r = 1; r < 16; ++r) {
+    mx1 = fmaxf(mx1, fmaxf(s1[0][r], s1[1][r]));
+    mx2 = fmaxf(mx2, fmaxf(s2[0][r], s2[1][r]));
   }
   const float m1n = fmaxf(m1, mx1), m2n = fmaxf(m2, mx2);
   const float a1 = exp2_hw((m1 - m1n) * c), a2 = exp2_hw((m2 - m2n) * c);
   const float nb1 = -m1n * c, nb2 = -m2n * c;
-  float sl1[4] = {0.f, 0.f, 0.f, 0.f}, sl2[4] = {0.f, 0.f, 0.f, 0.f}, sa[4] = {0.f, 0.f, 0.f, 0.f};
+  float sl1[2] = {0.f, 0.f}, sl2[2] = {0.f, 0.f}, sa[2] = {0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float p1 = exp2_hw(fmaf(e1[i], c, nb1));
-    const float p2 = exp2_hw(fmaf(e2[i], c, nb2));
-    sl1[i & 3] += p1;
-    sl2[i & 3] += p2;
-    sa[i & 3] = fmaf(p1, d12[i], sa[i & 3]);
-  }
-  l1 = fmaf(l1, a1, (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]));
-  l2 = fmaf(l2, a2, (sl2[0] + sl2[1]) + (sl2[2] + sl2[3]));
-  acc = fmaf(acc, a1, (sa[0] + sa[1]) + (sa[2] + sa[3]));
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x1 = s1[rb][r], x2 = s2[rb][r];
+      const float p1 = exp2_hw(fmaf(x1, c, nb1));
+      const float p2 = exp2_hw(fmaf(x2, c, nb2));
+      sl1[r & 1] += p1;
+      sl2[r & 1] += p2;
+      // masked entries have x1 = x2 = -inf and p1 = 0; their difference must not turn into NaN
+      const float dd = MASK ? (p1 > 0.f ? x1 - x2 : 0.f) : x1 - x2;
+      sa[r & 1] = fmaf(p1, dd, sa[r & 1]);
+    }
+  l1 = fmaf(l1, a1, sl1[0] + sl1[1]);
+  l2 = fmaf(l2, a2, sl2[0] + sl2[1]);
+  acc = fmaf(acc, a1, sa[0] + sa[1]);
   m1 = m1n;
   m2 = m2n;
 }
 
+constexpr int kFwdWaves = 8;
+constexpr int kFwdThreads = 64 * kFwdWaves;
+
+// Forward: a block of 8 waves covers 256 query rows of one slice (32 per wave) and streams
+// 64-key tiles of K1 and K2 through double-buffered LDS, one barrier per tile.
 template <int D, bool CAUSAL, bool SHARED_K>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kFwdThreads)
 fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
            const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
            float* __restrict__ kl_out, float* __restrict__ lse1_out,
            float* __restrict__ lse2_out, Shape s) {
-  constexpr int BQ = 32 * kWaves, BK = 64, KS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t lk1[BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t lk2[SHARED_K ? 8 : BK * D];
+  constexpr int BQ = 32 * kFwdWaves, BK = 64, KS = D / 16, NKT = SHARED_K ? 1 : 2;
+  constexpr int TILE = BK * lds_pitch<D>();
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * NKT * TILE];
 
   int rank, slice;
   block_coords(s.bh, rank, slice);
@@ -255,41 +237,59 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   const bool wave_live = qw0 < s.nq;
 
   float m1 = kNegBig, m2 = kNegBig, l1 = 0.f, l2 = 0.f, acc = 0.f;
-  TileRegs<BK, D> r1, r2;
+  TileRegs<BK, D, kFwdThreads> r1, r2;
   r1.load(K1, s.k_sr, 0, s.nk);
   if (!SHARED_K) r2.load(K2, s.k_sr, 0, s.nk);
+  r1.store(lds);
+  if (!SHARED_K) r2.store(lds + TILE);
+  if (ntiles > 1) {
+    r1.load(K1, s.k_sr, BK, s.nk);
+    if (!SHARED_K) r2.load(K2, s.k_sr, BK, s.nk);
+  }
+  __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    r1.store(lk1);
-    if (!SHARED_K) r2.store(lk2);
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      r1.load(K1, s.k_sr, (t + 1) * BK, s.nk);
-      if (!SHARED_K) r2.load(K2, s.k_sr, (t + 1) * BK, s.nk);
-    }
+    const uint16_t* kt1 = lds + (t & 1) * NKT * TILE;
+    const uint16_t* kt2 = kt1 + (NKT - 1) * TILE;
     const int key0 = t * BK;
-    if (!wave_live) continue;
-    if (CAUSAL && key0 > qw0 + 31) continue;  // every key of the tile is past this wave's rows
-    f32x16 s1[2], s2[2];
+    // every key of the tile is past this wave's rows: nothing to do for it
+    const bool skip = !wave_live || (CAUSAL && key0 > qw0 + 31);
+    if (!skip) {
+      f32x16 s1[2], s2[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      f32x16 x1 = {}, x2 = {};
+      for (int rb = 0; rb < 2; ++rb) {
+        bf16x8 a1[KS], a2[KS];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const bf16x8 a = lds_a_frag<D>(lk1, rb * 32 + col, kk, h);
-        x1 = mfma(a, f1[kk], x1);
-        const bf16x8 a2 = SHARED_K ? a : lds_a_frag<D>(lk2, rb * 32 + col, kk, h);
-        x2 = mfma(a2, f2[kk], x2);
+        for (int kk = 0; kk < KS; ++kk) {
+          a1[kk] = lds_a_frag<D>(kt1, rb * 32 + col, kk, h);
+          if (!SHARED_K) a2[kk] = lds_a_frag<D>(kt2, rb * 32 + col, kk, h);
+        }
+        f32x16 x1 = {}, x2 = {};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          x1 = mfma(a1[kk], f1[kk], x1);
+          x2 = mfma(SHARED_K ? a1[kk] : a2[kk], f2[kk], x2);
+        }
+        s1[rb] = x1;
+        s2[rb] = x2;
       }
-      s1[rb] = x1;
-      s2[rb] = x2;
+      const bool full = (key0 + BK <= s.nk) && (!CAUSAL || key0 + BK - 1 <= qw0);
+      if (full)
+        fwd_tile_update<CAUSAL, false>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+      else
+        fwd_tile_update<CAUSAL, true>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
     }
-    const bool full = (key0 + BK <= s.nk) && (!CAUSAL || key0 + BK - 1 <= qw0);
-    if (full)
-      fwd_tile_update<D, CAUSAL, false>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
-    else
-      fwd_tile_update<D, CAUSAL, true>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+    if (t + 1 < ntiles) {
+      // the other buffer was last read in iteration t - 1, before the previous barrier
+      uint16_t* nxt = lds + ((t + 1) & 1) * NKT * TILE;
+      r1.store(nxt);
+      if (!SHARED_K) r2.store(nxt + TILE);
+      if (t + 2 < ntiles) {
+        r1.load(K1, s.k_sr, (t + 2) * BK, s.nk);
+        if (!SHARED_K) r2.load(K2, s.k_sr, (t + 2) * BK, s.nk);
+      }
+    }
+    __syncthreads();
   }
 
   // Merge the two partial states of this query row (lanes l and l ^ 32).
@@ -312,18 +312,111 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   }
 }
 
-// ================================================================ backward: dQ (query-major)
+// ================================================================ backward
+// Both backward kernels stream 32-row tiles of the "other" side (key rows for the dQ kernel,
+// query rows for the dK kernel) through double-buffered LDS, one barrier per tile, with 8 waves
+// of 32 stationary rows each. A streamed tile is kept twice when it belongs to the free side:
+// row-major (operand of the S recomputation, contraction over head_dim) and transposed (operand
+// of the gradient product, contraction over the streamed rows). The transposed copy stores row r
+// of the tile at column tpos(r) (bits 2 and 3 of r swapped) so that lane half h of a 32x32x16
+// MFMA reads its eight rows 16c + {4h..4h+3, 8+4h..8+4h+3} as one contiguous 16-byte chunk:
+// the order in which a 32x32 accumulator holds rows (acc_row), which makes the accumulator of
+// dS directly the A operand of the gradient product.
+constexpr int kBwdWaves = 8;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBT = 32;              // streamed rows per tile
+constexpr int kTPitch = kBT + 8;     // pitch (elements) of a transposed tile
+
+__device__ __forceinline__ int tpos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <int D>
+struct BwdLayout {
+  static constexpr int RM = kBT * lds_pitch<D>();  // one row-major tile (elements)
+  static constexpr int TR = D * kTPitch;           // one transposed tile (elements)
+};
+
+// Staging of the NT streamed tensors of one tile (tensor 0 = side 1, tensor 1 = side 2; one
+// tensor when K is shared). Chunk assignment is column-major (row = id % 32) so that the two
+// rows of a pair (r, r ^ 1) sit in neighbouring lanes for the transposed store.
+template <int D, int NTENS>
+struct BwdStage {
+  static constexpr int CPR = D / 8;
+  static constexpr int PER = kBT * CPR;                          // chunks per tensor
+  static constexpr int N = (NTENS * PER + kBwdThreads - 1) / kBwdThreads;
+  uint4 v[N];
+
+  __device__ __forceinline__ bool mine(int i, int& te, int& row, int& chunk) const {
+    const int gid = threadIdx.x + i * kBwdThreads;
+    te = gid / PER;
+    const int rem = gid - te * PER;
+    row = rem % kBT;
+    chunk = rem / kBT;
+    return gid < NTENS * PER;
+  }
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ b0,
+                                       const uint16_t* __restrict__ b1, long long rstride,
+                                       int row0, int n_valid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int te, row, chunk;
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (mine(i, te, row, chunk) && row0 + row < n_valid)
+        v[i] = *reinterpret_cast<const uint4*>((te == 0 ? b0 : b1) +
+                                               (long long)(row0 + row) * rstride + chunk * 8);
+    }
+  }
+  // Row-major copies of every tensor; transposed copy of tensor `free_te`.
+  __device__ __forceinline__ void store(uint16_t* rm0, uint16_t* rm1, uint16_t* tr,
+                                        int free_te) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int te, row, chunk;
+      if (!mine(i, te, row, chunk)) continue;
+      uint16_t* rm = te == 0 ? rm0 : rm1;
+      *reinterpret_cast<uint4*>(rm + row * lds_pitch<D>() + chunk * 8) = v[i];
+      if (te == free_te) {
+        // lanes l (row r even) and l ^ 1 (row r + 1) swap their chunks; the even lane writes
+        // head_dim columns chunk*8 + 0..3, the odd one chunk*8 + 4..7, each as (r, r+1) pairs
+        const uint4 o = make_uint4(__shfl_xor(v[i].x, 1), __shfl_xor(v[i].y, 1),
+                                   __shfl_xor(v[i].z, 1), __shfl_xor(v[i].w, 1));
+        const bool odd = row & 1;
+        const uint4 lo = odd ? o : v[i];   // row r even
+        const uint4 hi = odd ? v[i] : o;   // row r + 1
+        const unsigned a0 = odd ? lo.z : lo.x, a1 = odd ? lo.w : lo.y;
+        const unsigned b0 = odd ? hi.z : hi.x, b1 = odd ? hi.w : hi.y;
+        const int d0 = chunk * 8 + (odd ? 4 : 0);
+        unsigned* t = reinterpret_cast<unsigned*>(tr + d0 * kTPitch + tpos(row & ~1));
+        constexpr int P = kTPitch / 2;  // pitch in dwords
+        t[0 * P] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+        t[1 * P] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+        t[2 * P] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+        t[3 * P] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+      }
+    }
+  }
+};
+
+// B operand of the gradient product: transposed tile rows (head_dim) nb*32 + (l & 31), the
+// eight streamed rows of chunk cc for lane half h.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tr, int nb, int cc, int col, int h) {
+  return load_frag(tr + (nb * 32 + col) * kTPitch + cc * 16 + h * 8);
+}
+
+// ---------------------------------------------------------------- dQ (query-major)
 template <int D, int SETTING, bool CAUSAL, bool SHARED_K>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kBwdThreads)
 dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
           const float* __restrict__ lse1, const float* __restrict__ lse2,
           const float* __restrict__ klv, const float* __restrict__ gv,
           __bf16* __restrict__ dq_out, Shape s) {
-  constexpr int BQ = 32 * kWaves, BT = 32, KS = D / 16, NB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t lk1[BT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t lk2[SHARED_K ? 8 : BT * D];
-  __shared__ float gscale[kWaves][32];
+  constexpr int BQ = 32 * kBwdWaves, KS = D / 16, NB = D / 32;
+  constexpr int NTENS = SHARED_K ? 1 : 2;
+  constexpr int FREE = SHARED_K ? 0 : 2 - SETTING;  // tensor index of K_free (side 2 for setting 1)
+  using L = BwdLayout<D>;
+  constexpr int BUF = NTENS * L::RM + L::TR;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
+  __shared__ float gscale[kBwdWaves][32];
 
   int rank, slice;
   block_coords(s.bh, rank, slice);
@@ -334,7 +427,6 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   const uint16_t* Q2 = q2 + b * s.q_sb + hd * s.q_sh;
   const uint16_t* K1 = k1 + b * s.k_sb + hd * s.k_sh;
   const uint16_t* K2 = k2 + b * s.k_sb + hd * s.k_sh;
-  const uint16_t* lkf = (SETTING == 1 && !SHARED_K) ? lk2 : lk1;  // free-side K tile
 
   const int l = lane_id(), w = wave_id(), h = l >> 5, col = l & 31;
   const int qw0 = qb * BQ + w * 32;
@@ -356,64 +448,74 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
 
   const int last_q = min(s.nq - 1, qb * BQ + BQ - 1);
   const int kend = CAUSAL ? min(s.nk, last_q + 1) : s.nk;
-  const int ntiles = (kend + BT - 1) / BT;
+  const int ntiles = (kend + kBT - 1) / kBT;
   const bool wave_live = qw0 < s.nq;
 
   f32x16 dq[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dq[nb] = f32x16{};
 
-  TileRegs<BT, D> r1, r2;
-  r1.load(K1, s.k_sr, 0, s.nk);
-  if (!SHARED_K) r2.load(K2, s.k_sr, 0, s.nk);
+  BwdStage<D, NTENS> st;
+  auto stage_store = [&](int buf) {
+    uint16_t* base = lds + buf * BUF;
+    st.store(base, base + (NTENS - 1) * L::RM, base + NTENS * L::RM, FREE);
+  };
+  st.load(K1, K2, s.k_sr, 0, s.nk);
+  stage_store(0);
+  if (ntiles > 1) st.load(K1, K2, s.k_sr, kBT, s.nk);
+  __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    r1.store(lk1);
-    if (!SHARED_K) r2.store(lk2);
-    __syncthreads();
+    const uint16_t* base = lds + (t & 1) * BUF;
+    const uint16_t* kt1 = base;
+    const uint16_t* kt2 = base + (NTENS - 1) * L::RM;
+    const uint16_t* ktr = base + NTENS * L::RM;
+    const int key0 = t * kBT;
+    const bool skip = !wave_live || (CAUSAL && key0 > qw0 + 31);
+    if (!skip) {
+      bf16x8 a1[KS], a2[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        a1[kk] = lds_a_frag<D>(kt1, col, kk, h);
+        if (!SHARED_K) a2[kk] = lds_a_frag<D>(kt2, col, kk, h);
+      }
+      f32x16 x1 = {}, x2 = {};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        x1 = mfma(a1[kk], f1[kk], x1);
+        x2 = mfma(SHARED_K ? a1[kk] : a2[kk], f2[kk], x2);
+      }
+      const bool full = (key0 + kBT <= s.nk) && (!CAUSAL || key0 + kBT - 1 <= qw0);
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e1 = x1[r], e2 = x2[r];
+        const float d12 = e1 - e2;
+        if (!full) {
+          const int key = key0 + acc_row(r, h);
+          const bool ok = key < s.nk && (!CAUSAL || key <= query);
+          e1 = ok ? e1 : -kInf;
+          e2 = ok ? e2 : -kInf;
+        }
+        const float p1 = exp2_hw(fmaf(e1, c, b1));
+        if (SETTING == 1)
+          ds[r] = exp2_hw(fmaf(e2, c, b2)) - p1;
+        else
+          ds[r] = p1 * fmaf(d12, s.scale, cst);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const bf16x8 a = pack8(ds + 8 * cc);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) dq[nb] = mfma(a, tr_frag(ktr, nb, cc, col, h), dq[nb]);
+      }
+    }
     if (t + 1 < ntiles) {
-      r1.load(K1, s.k_sr, (t + 1) * BT, s.nk);
-      if (!SHARED_K) r2.load(K2, s.k_sr, (t + 1) * BT, s.nk);
+      stage_store((t + 1) & 1);
+      if (t + 2 < ntiles) st.load(K1, K2, s.k_sr, (t + 2) * kBT, s.nk);
     }
-    const int key0 = t * BT;
-    if (!wave_live) continue;
-    if (CAUSAL && key0 > qw0 + 31) continue;
-    f32x16 x1 = {}, x2 = {};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8 a = lds_a_frag<D>(lk1, col, kk, h);
-      x1 = mfma(a, f1[kk], x1);
-      const bf16x8 a2 = SHARED_K ? a : lds_a_frag<D>(lk2, col, kk, h);
-      x2 = mfma(a2, f2[kk], x2);
-    }
-    const bool full = (key0 + BT <= s.nk) && (!CAUSAL || key0 + BT - 1 <= qw0);
-    float ds[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float e1 = x1[r], e2 = x2[r];
-      const float d12 = e1 - e2;
-      if (!full) {
-        const int key = key0 + acc_row(r, h);
-        const bool ok = key < s.nk && (!CAUSAL || key <= query);
-        e1 = ok ? e1 : -kInf;
-        e2 = ok ? e2 : -kInf;
-      }
-      const float p1 = exp2_hw(fmaf(e1, c, b1));
-      if (SETTING == 1) {
-        ds[r] = exp2_hw(fmaf(e2, c, b2)) - p1;
-      } else {
-        ds[r] = p1 * fmaf(d12, s.scale, cst);
-      }
-    }
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const bf16x8 a = pack8(ds + 8 * cc);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) dq[nb] = mfma(a, lds_bt_frag<D>(lkf, 16 * cc, nb * 32), dq[nb]);
-    }
+    __syncthreads();
   }
-  __syncthreads();
   if (!wave_live) return;
   const long long obase = (long long)slice * s.nq;
 #pragma unroll
@@ -428,20 +530,21 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   }
 }
 
-// ================================================================ backward: dK (key-major)
+// ---------------------------------------------------------------- dK (key-major)
 template <int D, int SETTING, bool CAUSAL, bool SHARED_K>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kBwdThreads)
 dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
           const float* __restrict__ lse1, const float* __restrict__ lse2,
           const float* __restrict__ klv, const float* __restrict__ gv,
           __bf16* __restrict__ dk_out, Shape s) {
-  constexpr int BKW = 32 * kWaves, BT = 32, KS = D / 16, NB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t lq1[BT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t lq2[BT * D];
-  // per query of the current tile: bias of P1, bias of P2 (setting 1) or the log-ratio
-  // constant LSE2 - LSE1 - KL (setting 2), and g
-  __shared__ __attribute__((aligned(16))) float qa[3][BT];
+  constexpr int BKW = 32 * kBwdWaves, KS = D / 16, NB = D / 32;
+  constexpr int FREE = 2 - SETTING;  // tensor index of Q_free (side 2 for setting 1)
+  using L = BwdLayout<D>;
+  constexpr int BUF = 2 * L::RM + L::TR;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
+  // per query of a tile: bias of P1, bias of P2 (setting 1) or LSE2 - LSE1 - KL (setting 2), g
+  __shared__ __attribute__((aligned(16))) float qa[2][3][kBT];
 
   int rank, slice;
   block_coords(s.bh, rank, slice);
@@ -451,7 +554,6 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   const uint16_t* Q2 = q2 + b * s.q_sb + hd * s.q_sh;
   const uint16_t* K1 = k1 + b * s.k_sb + hd * s.k_sh;
   const uint16_t* K2 = k2 + b * s.k_sb + hd * s.k_sh;
-  const uint16_t* lqf = SETTING == 1 ? lq2 : lq1;  // free-side Q tile
   const long long rbase = (long long)slice * s.nq;
 
   const int l = lane_id(), w = wave_id(), h = l >> 5, col = l & 31;
@@ -466,87 +568,112 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
     f2[kk] = SHARED_K ? f1[kk] : load_frag(K2 + (long long)krow * s.k_sr + kk * 16 + h * 8);
   }
   const float c = s.scale * kLog2e;
-  const int t0 = CAUSAL ? (kb * BKW) / BT : 0;
-  const int t1 = (s.nq + BT - 1) / BT;
+  // query tiles run from the last one down to the first visible one, so that the blocks of one
+  // slice, which start together, stream the same tiles at the same time
+  const int t_lo = CAUSAL ? (kb * BKW) / kBT : 0;
+  const int t_hi = (s.nq + kBT - 1) / kBT - 1;
   const bool wave_live = kw0 < s.nk;
 
   f32x16 dk[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dk[nb] = f32x16{};
 
-  TileRegs<BT, D> r1, r2;
-  if (t0 < t1) {
-    r1.load(Q1, s.q_sr, t0 * BT, s.nq);
-    r2.load(Q2, s.q_sr, t0 * BT, s.nq);
-  }
-  for (int t = t0; t < t1; ++t) {
-    __syncthreads();
-    r1.store(lq1);
-    r2.store(lq2);
-    if (threadIdx.x < BT) {
-      const int q = t * BT + threadIdx.x;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+  BwdStage<D, 2> st;
+  float cq0 = 0.f, cq1 = 0.f, cq2 = 0.f;  // constants of query tile row threadIdx.x (< kBT)
+  auto load_tile = [&](int t) {
+    st.load(Q1, Q2, s.q_sr, t * kBT, s.nq);
+    if (threadIdx.x < kBT) {
+      const int q = t * kBT + threadIdx.x;
+      cq0 = cq1 = cq2 = 0.f;  // rows past n_q: g = 0, so they contribute nothing
       if (q < s.nq) {
         const float x1 = lse1[rbase + q], x2 = lse2[rbase + q];
-        a0 = -x1 * kLog2e;
-        a1 = SETTING == 1 ? -x2 * kLog2e : (x2 - x1) - klv[rbase + q];
-        a2 = gv[rbase + q];
+        cq0 = -x1 * kLog2e;
+        cq1 = SETTING == 1 ? -x2 * kLog2e : (x2 - x1) - klv[rbase + q];
+        cq2 = gv[rbase + q];
       }
-      qa[0][threadIdx.x] = a0;
-      qa[1][threadIdx.x] = a1;
-      qa[2][threadIdx.x] = a2;
+    }
+  };
+  auto stage_store = [&](int buf) {
+    uint16_t* base = lds + buf * BUF;
+    st.store(base, base + L::RM, base + 2 * L::RM, FREE);
+    if (threadIdx.x < kBT) {
+      qa[buf][0][threadIdx.x] = cq0;
+      qa[buf][1][threadIdx.x] = cq1;
+      qa[buf][2][threadIdx.x] = cq2;
+    }
+  };
+  const int ntiles = t_hi >= t_lo ? t_hi - t_lo + 1 : 0;
+  if (ntiles > 0) {
+    load_tile(t_hi);
+    stage_store(0);
+    if (ntiles > 1) load_tile(t_hi - 1);
+  }
+  __syncthreads();
+
+  for (int i = 0; i < ntiles; ++i) {
+    const int t = t_hi - i;
+    const int buf = i & 1;
+    const uint16_t* base = lds + buf * BUF;
+    const uint16_t* qt1 = base;
+    const uint16_t* qt2 = base + L::RM;
+    const uint16_t* qtr = base + 2 * L::RM;
+    const int qt0 = t * kBT;
+    const bool skip = !wave_live || (CAUSAL && qt0 + kBT - 1 < kw0);
+    if (!skip) {
+      bf16x8 a1[KS], a2[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        a1[kk] = lds_a_frag<D>(qt1, col, kk, h);
+        a2[kk] = lds_a_frag<D>(qt2, col, kk, h);
+      }
+      f32x16 x1 = {}, x2 = {};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        x1 = mfma(a1[kk], f1[kk], x1);
+        x2 = mfma(a2[kk], f2[kk], x2);
+      }
+      const bool full = (qt0 + kBT <= s.nq) && (!CAUSAL || qt0 >= kw0 + 31);
+      float ds[16];
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        // registers 4rq..4rq+3 hold 4 consecutive queries
+        const int qi = rq * 8 + h * 4;
+        const float4 va0 = *reinterpret_cast<const float4*>(&qa[buf][0][qi]);
+        const float4 va1 = *reinterpret_cast<const float4*>(&qa[buf][1][qi]);
+        const float4 va2 = *reinterpret_cast<const float4*>(&qa[buf][2][qi]);
+        const float c0[4] = {va0.x, va0.y, va0.z, va0.w};
+        const float c1[4] = {va1.x, va1.y, va1.z, va1.w};
+        const float c2[4] = {va2.x, va2.y, va2.z, va2.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = rq * 4 + j;
+          float e1 = x1[r], e2 = x2[r];
+          const float d12 = e1 - e2;
+          if (!full) {
+            const int q = qt0 + qi + j;
+            const bool ok = q < s.nq && (!CAUSAL || key <= q);
+            e1 = ok ? e1 : -kInf;
+            e2 = ok ? e2 : -kInf;
+          }
+          const float p1 = exp2_hw(fmaf(e1, c, c0[j]));
+          if (SETTING == 1)
+            ds[r] = c2[j] * (exp2_hw(fmaf(e2, c, c1[j])) - p1);
+          else
+            ds[r] = c2[j] * (p1 * fmaf(d12, s.scale, c1[j]));
+        }
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const bf16x8 a = pack8(ds + 8 * cc);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) dk[nb] = mfma(a, tr_frag(qtr, nb, cc, col, h), dk[nb]);
+      }
+    }
+    if (i + 1 < ntiles) {
+      stage_store(buf ^ 1);
+      if (i + 2 < ntiles) load_tile(t - 2);
     }
     __syncthreads();
-    if (t + 1 < t1) {
-      r1.load(Q1, s.q_sr, (t + 1) * BT, s.nq);
-      r2.load(Q2, s.q_sr, (t + 1) * BT, s.nq);
-    }
-    const int qt0 = t * BT;
-    if (!wave_live) continue;
-    if (CAUSAL && qt0 + BT - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
-    f32x16 x1 = {}, x2 = {};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      x1 = mfma(lds_a_frag<D>(lq1, col, kk, h), f1[kk], x1);
-      x2 = mfma(lds_a_frag<D>(lq2, col, kk, h), f2[kk], x2);
-    }
-    const bool full = (qt0 + BT <= s.nq) && (!CAUSAL || qt0 >= kw0 + 31);
-    float ds[16];
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      // registers 4rq..4rq+3 hold 4 consecutive queries
-      const int qi = rq * 8 + h * 4;
-      const float4 va0 = *reinterpret_cast<const float4*>(&qa[0][qi]);
-      const float4 va1 = *reinterpret_cast<const float4*>(&qa[1][qi]);
-      const float4 va2 = *reinterpret_cast<const float4*>(&qa[2][qi]);
-      const float c0[4] = {va0.x, va0.y, va0.z, va0.w};
-      const float c1[4] = {va1.x, va1.y, va1.z, va1.w};
-      const float c2[4] = {va2.x, va2.y, va2.z, va2.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = rq * 4 + j;
-        float e1 = x1[r], e2 = x2[r];
-        const float d12 = e1 - e2;
-        if (!full) {
-          const int q = qt0 + qi + j;
-          const bool ok = q < s.nq && (!CAUSAL || key <= q);
-          e1 = ok ? e1 : -kInf;
-          e2 = ok ? e2 : -kInf;
-        }
-        const float p1 = exp2_hw(fmaf(e1, c, c0[j]));
-        if (SETTING == 1) {
-          ds[r] = c2[j] * (exp2_hw(fmaf(e2, c, c1[j])) - p1);
-        } else {
-          ds[r] = c2[j] * (p1 * fmaf(d12, s.scale, c1[j]));
-        }
-      }
-    }
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const bf16x8 a = pack8(ds + 8 * cc);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) dk[nb] = mfma(a, lds_bt_frag<D>(lqf, 16 * cc, nb * 32), dk[nb]);
-    }
   }
   if (!wave_live) return;
   const long long obase = (long long)slice * s.nk;
@@ -655,8 +782,8 @@ streamkl_status_t check_launch(const char* what) {
 template <int D, bool CAUSAL, bool SK>
 void launch_fwd(const Shape& s, const void* q1, const void* k1, const void* q2, const void* k2,
                 float* kl, float* l1, float* l2, hipStream_t st) {
-  const int nqb = (s.nq + 128 - 1) / 128;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SK>), dim3(nqb * s.bh), dim3(kThreads), 0, st,
+  const int nqb = (s.nq + 32 * kFwdWaves - 1) / (32 * kFwdWaves);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SK>), dim3(nqb * s.bh), dim3(kFwdThreads), 0, st,
                      (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
                      (const uint16_t*)k2, kl, l1, l2, s);
 }
@@ -665,14 +792,14 @@ template <int D, int SET, bool CAUSAL, bool SK>
 void launch_bwd(const Shape& s, const void* q1, const void* k1, const void* q2, const void* k2,
                 const float* l1, const float* l2, const float* kl, const float* g, void* dq,
                 void* dk, hipStream_t st) {
-  const int nqb = (s.nq + 128 - 1) / 128;
-  const int nkb = (s.nk + 128 - 1) / 128;
+  const int nqb = (s.nq + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
+  const int nkb = (s.nk + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
   if (dq)
-    hipLaunchKernelGGL((dq_kernel<D, SET, CAUSAL, SK>), dim3(nqb * s.bh), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((dq_kernel<D, SET, CAUSAL, SK>), dim3(nqb * s.bh), dim3(kBwdThreads), 0, st,
                        (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
                        (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dq, s);
   if (dk)
-    hipLaunchKernelGGL((dk_kernel<D, SET, CAUSAL, SK>), dim3(nkb * s.bh), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((dk_kernel<D, SET, CAUSAL, SK>), dim3(nkb * s.bh), dim3(kBwdThreads), 0, st,
                        (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
                        (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dk, s);
 }

@@ -24,6 +24,9 @@ def build_library(verbose: bool = False) -> str:
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
            # packed fp32 VALU forms are kept out of the generated code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # no NaN semantics: lets fmaxf map to v_max3_f32 without canonicalising MFMA results
+           # (infinities, used for masking, are still honoured)
+           "-fno-honor-nans",
            "-I", os.path.join(ROOT, "include"), "-o", tmp] + SOURCES
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

@@ -166,46 +166,68 @@ __device__ __forceinline__ void fwd_tile_update(f32x16 (&s1)[2], f32x16 (&s2)[2]
   float mx1 = fmaxf(s1[0][0], s1[1][0]), mx2 = fmaxf(s2[0][0], s2[1][0]);
 #pragma unroll
   for (int r = 1; r < 16; ++r) {
-    mx1 = fmaxf(mx1, fmaxf(s1[0][r], s1[1][r]));
-    mx2 = fmaxf(mx2, fmaxf(s2[0][r], s2[1][r]));
+    mx1 = fmaxf(fmaxf(mx1, s1[0][r]), s1[1][r]);
+    mx2 = fmaxf(fmaxf(mx2, s2[0][r]), s2[1][r]);
   }
   const float m1n = fmaxf(m1, mx1), m2n = fmaxf(m2, mx2);
   const float a1 = exp2_hw((m1 - m1n) * c), a2 = exp2_hw((m2 - m2n) * c);
   const float nb1 = -m1n * c, nb2 = -m2n * c;
-  float sl1[2] = {0.f, 0.f}, sl2[2] = {0.f, 0.f}, sa[2] = {0.f, 0.f};
+  float sl1[4], sl2[4], sa[4];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < 2; ++rb) {
+    float p1[16], p2[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p1[r] = exp2_hw(fmaf(s1[rb][r], c, nb1));
+      p2[r] = exp2_hw(fmaf(s2[rb][r], c, nb2));
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float x1 = s1[rb][r], x2 = s2[rb][r];
-      const float p1 = exp2_hw(fmaf(x1, c, nb1));
-      const float p2 = exp2_hw(fmaf(x2, c, nb2));
-      sl1[r & 1] += p1;
-      sl2[r & 1] += p2;
       // masked entries have x1 = x2 = -inf and p1 = 0; their difference must not turn into NaN
-      const float dd = MASK ? (p1 > 0.f ? x1 - x2 : 0.f) : x1 - x2;
-      sa[r & 1] = fmaf(p1, dd, sa[r & 1]);
+      const float dd = MASK ? (p1[r] > 0.f ? x1 - x2 : 0.f) : x1 - x2;
+      const int j = r & 3;
+      if (rb == 0 && r < 4) {
+        sl1[j] = p1[r];
+        sl2[j] = p2[r];
+        sa[j] = p1[r] * dd;
+      } else {
+        sl1[j] += p1[r];
+        sl2[j] += p2[r];
+        sa[j] = fmaf(p1[r], dd, sa[j]);
+      }
     }
-  l1 = fmaf(l1, a1, sl1[0] + sl1[1]);
-  l2 = fmaf(l2, a2, sl2[0] + sl2[1]);
-  acc = fmaf(acc, a1, sa[0] + sa[1]);
+    if (!MASK) {
+      // issue order for the machine scheduler: all exponent arguments, then all exponentials,
+      // then the sums, so that no instruction waits on the one just before it
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // 32 FMAs (VALU)
+      __builtin_amdgcn_sched_group_barrier(0x400, 32, 0);  // 32 exp (transcendental)
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);  // differences, sums, acc
+    }
+  }
+  l1 = fmaf(l1, a1, (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]));
+  l2 = fmaf(l2, a2, (sl2[0] + sl2[1]) + (sl2[2] + sl2[3]));
+  acc = fmaf(acc, a1, (sa[0] + sa[1]) + (sa[2] + sa[3]));
   m1 = m1n;
   m2 = m2n;
 }
 
 constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
+constexpr int kFwdBlocksPerCU = 8 / kFwdWaves;  // 2 waves per SIMD
 
 // Forward: a block of 8 waves covers 256 query rows of one slice (32 per wave) and streams
 // 64-key tiles of K1 and K2 through double-buffered LDS, one barrier per tile.
 template <int D, bool CAUSAL, bool SHARED_K>
-__global__ void __launch_bounds__(kFwdThreads)
+__global__ void __launch_bounds__(kFwdThreads, kFwdBlocksPerCU)
 fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
            const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
            float* __restrict__ kl_out, float* __restrict__ lse1_out,
            float* __restrict__ lse2_out, Shape s) {
-  constexpr int BQ = 32 * kFwdWaves, BK = 64, KS = D / 16, NKT = SHARED_K ? 1 : 2;
-  constexpr int TILE = BK * lds_pitch<D>();
+  // LDS holds stages of SB = 128 keys (double-buffered); each stage is consumed as two 64-key
+  // tiles, so that one barrier and one staging pass serve 64 MFMAs per wave
+  constexpr int BQ = 32 * kFwdWaves, BK = 64, SB = 128, KS = D / 16, NKT = SHARED_K ? 1 : 2;
+  constexpr int TILE = SB * lds_pitch<D>();
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * NKT * TILE];
 
   int rank, slice;
@@ -233,60 +255,72 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   const int last_q = min(s.nq - 1, qb * BQ + BQ - 1);
   const int kend = CAUSAL ? min(s.nk, last_q + 1) : s.nk;
   const int ntiles = (kend + BK - 1) / BK;
+  const int nstages = (kend + SB - 1) / SB;
   const float c = s.scale * kLog2e;
   const bool wave_live = qw0 < s.nq;
 
   float m1 = kNegBig, m2 = kNegBig, l1 = 0.f, l2 = 0.f, acc = 0.f;
-  TileRegs<BK, D, kFwdThreads> r1, r2;
+  TileRegs<SB, D, kFwdThreads> r1, r2;
   r1.load(K1, s.k_sr, 0, s.nk);
   if (!SHARED_K) r2.load(K2, s.k_sr, 0, s.nk);
   r1.store(lds);
   if (!SHARED_K) r2.store(lds + TILE);
-  if (ntiles > 1) {
-    r1.load(K1, s.k_sr, BK, s.nk);
-    if (!SHARED_K) r2.load(K2, s.k_sr, BK, s.nk);
+  if (nstages > 1) {
+    r1.load(K1, s.k_sr, SB, s.nk);
+    if (!SHARED_K) r2.load(K2, s.k_sr, SB, s.nk);
   }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const uint16_t* kt1 = lds + (t & 1) * NKT * TILE;
-    const uint16_t* kt2 = kt1 + (NKT - 1) * TILE;
-    const int key0 = t * BK;
-    // every key of the tile is past this wave's rows: nothing to do for it
-    const bool skip = !wave_live || (CAUSAL && key0 > qw0 + 31);
-    if (!skip) {
-      f32x16 s1[2], s2[2];
+  f32x16 s1[2], s2[2];
+  // S^T of the 64-key tile starting at row `row0` of the stage in LDS: four independent
+  // accumulation chains (2 key blocks x 2 distributions)
+  auto contract = [&](const uint16_t* kt1, const uint16_t* kt2, int row0) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      s1[rb] = f32x16{};
+      s2[rb] = f32x16{};
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      bf16x8 a1[2], a2[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        bf16x8 a1[KS], a2[KS];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          a1[kk] = lds_a_frag<D>(kt1, rb * 32 + col, kk, h);
-          if (!SHARED_K) a2[kk] = lds_a_frag<D>(kt2, rb * 32 + col, kk, h);
-        }
-        f32x16 x1 = {}, x2 = {};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          x1 = mfma(a1[kk], f1[kk], x1);
-          x2 = mfma(SHARED_K ? a1[kk] : a2[kk], f2[kk], x2);
-        }
-        s1[rb] = x1;
-        s2[rb] = x2;
+        a1[rb] = lds_a_frag<D>(kt1, row0 + rb * 32 + col, kk, h);
+        if (!SHARED_K) a2[rb] = lds_a_frag<D>(kt2, row0 + rb * 32 + col, kk, h);
       }
-      const bool full = (key0 + BK <= s.nk) && (!CAUSAL || key0 + BK - 1 <= qw0);
-      if (full)
-        fwd_tile_update<CAUSAL, false>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
-      else
-        fwd_tile_update<CAUSAL, true>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        s1[rb] = mfma(a1[rb], f1[kk], s1[rb]);
+        s2[rb] = mfma(SHARED_K ? a1[rb] : a2[rb], f2[kk], s2[rb]);
+      }
     }
-    if (t + 1 < ntiles) {
-      // the other buffer was last read in iteration t - 1, before the previous barrier
-      uint16_t* nxt = lds + ((t + 1) & 1) * NKT * TILE;
+  };
+
+  for (int st = 0; st < nstages; ++st) {
+    const uint16_t* kt1 = lds + (st & 1) * NKT * TILE;
+    const uint16_t* kt2 = kt1 + (NKT - 1) * TILE;
+#pragma unroll
+    for (int sub = 0; sub < SB / BK; ++sub) {
+      const int t = st * (SB / BK) + sub;
+      const int key0 = t * BK;
+      // a tile is skipped when it is past the end or every key of it is past this wave's rows
+      if (t < ntiles && wave_live && !(CAUSAL && key0 > qw0 + 31)) {
+        contract(kt1, kt2, sub * BK);
+        const bool full = (key0 + BK <= s.nk) && (!CAUSAL || key0 + BK - 1 <= qw0);
+        if (full)
+          fwd_tile_update<CAUSAL, false>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+        else
+          fwd_tile_update<CAUSAL, true>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+      }
+    }
+    if (st + 1 < nstages) {
+      // the other buffer was last read in stage st - 1, before the previous barrier
+      uint16_t* nxt = lds + ((st + 1) & 1) * NKT * TILE;
       r1.store(nxt);
       if (!SHARED_K) r2.store(nxt + TILE);
-      if (t + 2 < ntiles) {
-        r1.load(K1, s.k_sr, (t + 2) * BK, s.nk);
-        if (!SHARED_K) r2.load(K2, s.k_sr, (t + 2) * BK, s.nk);
+      if (st + 2 < nstages) {
+        r1.load(K1, s.k_sr, (st + 2) * SB, s.nk);
+        if (!SHARED_K) r2.load(K2, s.k_sr, (st + 2) * SB, s.nk);
       }
     }
     __syncthreads();
@@ -324,6 +358,7 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
 // dS directly the A operand of the gradient product.
 constexpr int kBwdWaves = 8;
 constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdBlocksPerCU = 8 / kBwdWaves;  // 2 waves per SIMD
 constexpr int kBT = 32;              // streamed rows per tile
 constexpr int kTPitch = kBT + 8;     // pitch (elements) of a transposed tile
 
@@ -404,7 +439,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tr, int nb, int cc, in
 
 // ---------------------------------------------------------------- dQ (query-major)
 template <int D, int SETTING, bool CAUSAL, bool SHARED_K>
-__global__ void __launch_bounds__(kBwdThreads)
+__global__ void __launch_bounds__(kBwdThreads, kBwdBlocksPerCU)
 dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
           const float* __restrict__ lse1, const float* __restrict__ lse2,
@@ -532,7 +567,7 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
 
 // ---------------------------------------------------------------- dK (key-major)
 template <int D, int SETTING, bool CAUSAL, bool SHARED_K>
-__global__ void __launch_bounds__(kBwdThreads)
+__global__ void __launch_bounds__(kBwdThreads, kBwdBlocksPerCU)
 dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
           const float* __restrict__ lse1, const float* __restrict__ lse2,

@@ -143,34 +143,37 @@ def backward_slice(setting: int, q1, k1, q2, k2, g, scale: float, causal: bool, 
 
 
 def dk_rows_slice(setting: int, q1, k1, q2, k2, g, scale: float, causal: bool, keys,
-                  fwd=None):
+                  fwd=None, rows=None):
     """dK_free[keys] (float64) of one slice, formed column by column.
 
-    Needs LSE1, LSE2 (and KL for setting 2) of every query row: taken from `fwd`
-    (= forward_slice(...) of this slice, all rows) or computed here.
+    Sums the contributions of query rows `rows` (all rows if None). Needs LSE1, LSE2 (and KL
+    for setting 2) of those rows: taken from `fwd` (= forward_slice(..., rows=rows)) or computed
+    here. With causal, a key j is seen only by rows i >= j, so for keys >= rows[0] a row set
+    that runs from rows[0] to the end gives the complete dK of those keys.
     """
     keys = np.asarray(keys)
-    if fwd is None:
-        fwd = forward_slice(q1, k1, q2, k2, scale, causal)
-    kl, lse1, lse2 = fwd
     n_q = q1.shape[0]
+    rows = np.arange(n_q) if rows is None else np.asarray(rows)
+    if fwd is None:
+        fwd = forward_slice(q1, k1, q2, k2, scale, causal, rows=rows)
+    kl, lse1, lse2 = fwd
     qf = q2 if setting == 1 else q1
-    S1 = scale * (np.asarray(q1, np.float64) @ np.asarray(k1[keys], np.float64).T)  # [N_Q, nkeys]
-    S2 = scale * (np.asarray(q2, np.float64) @ np.asarray(k2[keys], np.float64).T)
+    S1 = scale * (np.asarray(q1[rows], np.float64) @ np.asarray(k1[keys], np.float64).T)
+    S2 = scale * (np.asarray(q2[rows], np.float64) @ np.asarray(k2[keys], np.float64).T)
     if causal:
-        vis = keys[None, :] <= np.arange(n_q)[:, None]
+        vis = keys[None, :] <= rows[:, None]
     else:
         vis = np.ones(S1.shape, dtype=bool)
     with np.errstate(invalid="ignore"):
         logp1 = np.where(vis, S1 - lse1[:, None], -np.inf)
         logp2 = np.where(vis, S2 - lse2[:, None], -np.inf)
         p1 = np.exp(logp1)
-        g = np.asarray(g, np.float64)[:, None]
+        gr = np.asarray(g, np.float64)[rows][:, None]
         if setting == 1:
-            dS = g * (np.exp(logp2) - p1)
+            dS = gr * (np.exp(logp2) - p1)
         else:
-            dS = g * p1 * np.where(vis, logp1 - logp2 - kl[:, None], 0.0)
-    return scale * (dS.T @ np.asarray(qf, np.float64))
+            dS = gr * p1 * np.where(vis, logp1 - logp2 - kl[:, None], 0.0)
+    return scale * (dS.T @ np.asarray(qf[rows], np.float64))
 
 
 # ---------------------------------------------------------------- whole tensors

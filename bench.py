@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--workload", default="causal_64k_d128", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain device copy of 1 GiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the StreamKL path here runs on a single MI355X "
@@ -146,6 +148,14 @@ def main():
     kl, l1, l2 = (torch.empty((B, H, nq), **f32) for _ in range(3))
     grads = {s: (torch.empty(q1.shape, dtype=torch.bfloat16, device=dev),
                  torch.empty(k1.shape, dtype=torch.bfloat16, device=dev)) for s in w.settings}
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        flush = torch.empty(1 << 30, dtype=torch.float32, device=dev).fill_(2.0)  # 4 GiB: evicts L2/MALL
+        torch.cuda.synchronize()
+        dst.copy_(src)          # reads 1 GiB and writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst, flush
     base_bytes = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
 

@@ -108,13 +108,15 @@ struct TileRegs {
   // Rows row0.. of a [n_valid, D] matrix with row stride rstride; rows >= n_valid read as 0.
   __device__ __forceinline__ void load(const uint16_t* __restrict__ base, long long rstride,
                                        int row0, int n_valid) {
+    const bool full = row0 + ROWS <= n_valid;  // block-uniform: no per-row checks needed
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int idx = threadIdx.x + i * NT;
       const int row = idx / CPR, c = idx % CPR;
       const int gr = row0 + row;
-      if (gr < n_valid)
-        v[i] = *reinterpret_cast<const uint4*>(base + (long long)gr * rstride + c * 8);
+      const uint16_t* src = base + (long long)gr * rstride + c * 8;
+      if (full || gr < n_valid)
+        v[i] = *reinterpret_cast<const uint4*>(src);
       else
         v[i] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -364,6 +366,11 @@ constexpr int kTPitch = kBT + 8;     // pitch (elements) of a transposed tile
 
 __device__ __forceinline__ int tpos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Value of lane l ^ 1 (DPP quad permutation [1, 0, 3, 2]: a VALU move, no LDS round trip).
+__device__ __forceinline__ unsigned swap_pair(unsigned x) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+}
+
 template <int D>
 struct BwdLayout {
   static constexpr int RM = kBT * lds_pitch<D>();  // one row-major tile (elements)
@@ -391,13 +398,15 @@ struct BwdStage {
   __device__ __forceinline__ void load(const uint16_t* __restrict__ b0,
                                        const uint16_t* __restrict__ b1, long long rstride,
                                        int row0, int n_valid) {
+    const bool full = row0 + kBT <= n_valid;  // block-uniform: no per-row checks needed
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       int te, row, chunk;
-      v[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (mine(i, te, row, chunk) && row0 + row < n_valid)
-        v[i] = *reinterpret_cast<const uint4*>((te == 0 ? b0 : b1) +
-                                               (long long)(row0 + row) * rstride + chunk * 8);
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (mine(i, te, row, chunk) && (full || row0 + row < n_valid))
+        val = *reinterpret_cast<const uint4*>((te == 0 ? b0 : b1) +
+                                              (long long)(row0 + row) * rstride + chunk * 8);
+      v[i] = val;
     }
   }
   // Row-major copies of every tensor; transposed copy of tensor `free_te`.
@@ -412,8 +421,8 @@ struct BwdStage {
       if (te == free_te) {
         // lanes l (row r even) and l ^ 1 (row r + 1) swap their chunks; the even lane writes
         // head_dim columns chunk*8 + 0..3, the odd one chunk*8 + 4..7, each as (r, r+1) pairs
-        const uint4 o = make_uint4(__shfl_xor(v[i].x, 1), __shfl_xor(v[i].y, 1),
-                                   __shfl_xor(v[i].z, 1), __shfl_xor(v[i].w, 1));
+        const uint4 o = make_uint4(swap_pair(v[i].x), swap_pair(v[i].y), swap_pair(v[i].z),
+                                   swap_pair(v[i].w));
         const bool odd = row & 1;
         const uint4 lo = odd ? o : v[i];   // row r even
         const uint4 hi = odd ? v[i] : o;   // row r + 1

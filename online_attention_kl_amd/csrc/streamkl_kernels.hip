@@ -148,15 +148,16 @@ __device__ __forceinline__ void block_coords(int n_slices, int& rank, int& slice
 }
 
 // ================================================================ forward
-// One key tile's contribution to a lane's partial online state. s1 / s2 hold the lane's 32
-// unscaled dot products of the tile (two 32-key blocks x 16 keys) and are masked in place.
-template <bool CAUSAL, bool MASK>
-__device__ __forceinline__ void fwd_tile_update(f32x16 (&s1)[2], f32x16 (&s2)[2], float c,
+// One key tile's contribution to a lane's partial online state. s1 / s2 hold the lane's
+// unscaled dot products of the tile (RB blocks of 32 keys, 16 keys of each block per lane) and
+// are masked in place.
+template <int RB, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void fwd_tile_update(f32x16 (&s1)[RB], f32x16 (&s2)[RB], float c,
                                                 int key0, int query, int nk, int h, float& m1,
                                                 float& l1, float& m2, float& l2, float& acc) {
   if (MASK) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + rb * 32 + acc_row(r, h);
@@ -165,46 +166,41 @@ __device__ __forceinline__ void fwd_tile_update(f32x16 (&s1)[2], f32x16 (&s2)[2]
         s2[rb][r] = ok ? s2[rb][r] : -kInf;
       }
   }
-  float mx1 = fmaxf(s1[0][0], s1[1][0]), mx2 = fmaxf(s2[0][0], s2[1][0]);
+  float mx1 = s1[0][0], mx2 = s2[0][0];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) {
-    mx1 = fmaxf(fmaxf(mx1, s1[0][r]), s1[1][r]);
-    mx2 = fmaxf(fmaxf(mx2, s2[0][r]), s2[1][r]);
+  for (int i = 1; i < 16 * RB; i += 2) {
+    const int rb = i / 16, r = i % 16, rb2 = (i + 1) / 16, r2 = (i + 1) % 16;
+    if (i + 1 < 16 * RB) {
+      mx1 = fmaxf(fmaxf(mx1, s1[rb][r]), s1[rb2][r2]);
+      mx2 = fmaxf(fmaxf(mx2, s2[rb][r]), s2[rb2][r2]);
+    } else {
+      mx1 = fmaxf(mx1, s1[rb][r]);
+      mx2 = fmaxf(mx2, s2[rb][r]);
+    }
   }
   const float m1n = fmaxf(m1, mx1), m2n = fmaxf(m2, mx2);
   const float a1 = exp2_hw((m1 - m1n) * c), a2 = exp2_hw((m2 - m2n) * c);
   const float nb1 = -m1n * c, nb2 = -m2n * c;
   float sl1[4], sl2[4], sa[4];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    float p1[16], p2[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p1[r] = exp2_hw(fmaf(s1[rb][r], c, nb1));
-      p2[r] = exp2_hw(fmaf(s2[rb][r], c, nb2));
-    }
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float x1 = s1[rb][r], x2 = s2[rb][r];
+      const float p1 = exp2_hw(fmaf(x1, c, nb1));
+      const float p2 = exp2_hw(fmaf(x2, c, nb2));
       // masked entries have x1 = x2 = -inf and p1 = 0; their difference must not turn into NaN
-      const float dd = MASK ? (p1[r] > 0.f ? x1 - x2 : 0.f) : x1 - x2;
+      const float dd = MASK ? (p1 > 0.f ? x1 - x2 : 0.f) : x1 - x2;
       const int j = r & 3;
       if (rb == 0 && r < 4) {
-        sl1[j] = p1[r];
-        sl2[j] = p2[r];
-        sa[j] = p1[r] * dd;
+        sl1[j] = p1;
+        sl2[j] = p2;
+        sa[j] = p1 * dd;
       } else {
-        sl1[j] += p1[r];
-        sl2[j] += p2[r];
-        sa[j] = fmaf(p1[r], dd, sa[j]);
+        sl1[j] += p1;
+        sl2[j] += p2;
+        sa[j] = fmaf(p1, dd, sa[j]);
       }
-    }
-    if (!MASK) {
-      // issue order for the machine scheduler: all exponent arguments, then all exponentials,
-      // then the sums, so that no instruction waits on the one just before it
-      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // 32 FMAs (VALU)
-      __builtin_amdgcn_sched_group_barrier(0x400, 32, 0);  // 32 exp (transcendental)
-      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);  // differences, sums, acc
     }
   }
   l1 = fmaf(l1, a1, (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]));
@@ -214,21 +210,25 @@ __device__ __forceinline__ void fwd_tile_update(f32x16 (&s1)[2], f32x16 (&s2)[2]
   m2 = m2n;
 }
 
+// Forward launch shape: blocks of kFwdWaves waves (32 query rows each), kFwdBlocksPerCU blocks
+// resident per CU, key tiles of 32 * kFwdRB rows, LDS stages of kFwdSB rows (double-buffered).
+// The softmax-style update is VALU-bound and a single wave issues VALU instructions at a
+// fraction of the SIMD's rate, so the shape favours several resident waves per SIMD.
 constexpr int kFwdWaves = 8;
+constexpr int kFwdBlocksPerCU = 1;
+constexpr int kFwdRB = 1;
+constexpr int kFwdSB = 64;
 constexpr int kFwdThreads = 64 * kFwdWaves;
-constexpr int kFwdBlocksPerCU = 8 / kFwdWaves;  // 2 waves per SIMD
 
-// Forward: a block of 8 waves covers 256 query rows of one slice (32 per wave) and streams
-// 64-key tiles of K1 and K2 through double-buffered LDS, one barrier per tile.
 template <int D, bool CAUSAL, bool SHARED_K>
 __global__ void __launch_bounds__(kFwdThreads, kFwdBlocksPerCU)
 fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
            const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
            float* __restrict__ kl_out, float* __restrict__ lse1_out,
            float* __restrict__ lse2_out, Shape s) {
-  // LDS holds stages of SB = 128 keys (double-buffered); each stage is consumed as two 64-key
-  // tiles, so that one barrier and one staging pass serve 64 MFMAs per wave
-  constexpr int BQ = 32 * kFwdWaves, BK = 64, SB = 128, KS = D / 16, NKT = SHARED_K ? 1 : 2;
+  constexpr int RB = kFwdRB, BK = 32 * RB, SB = kFwdSB, BQ = 32 * kFwdWaves, KS = D / 16;
+  constexpr int NKT = SHARED_K ? 1 : 2;
+  static_assert(SB % BK == 0, "a stage holds whole tiles");
   constexpr int TILE = SB * lds_pitch<D>();
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * NKT * TILE];
 
@@ -273,25 +273,24 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   }
   __syncthreads();
 
-  f32x16 s1[2], s2[2];
-  // S^T of the 64-key tile starting at row `row0` of the stage in LDS: four independent
-  // accumulation chains (2 key blocks x 2 distributions)
+  f32x16 s1[RB], s2[RB];
+  // S^T of the tile starting at row `row0` of the stage: 2 * RB independent accumulation chains
   auto contract = [&](const uint16_t* kt1, const uint16_t* kt2, int row0) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       s1[rb] = f32x16{};
       s2[rb] = f32x16{};
     }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      bf16x8 a1[2], a2[2];
+      bf16x8 a1[RB], a2[RB];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
         a1[rb] = lds_a_frag<D>(kt1, row0 + rb * 32 + col, kk, h);
         if (!SHARED_K) a2[rb] = lds_a_frag<D>(kt2, row0 + rb * 32 + col, kk, h);
       }
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
         s1[rb] = mfma(a1[rb], f1[kk], s1[rb]);
         s2[rb] = mfma(SHARED_K ? a1[rb] : a2[rb], f2[kk], s2[rb]);
       }
@@ -310,9 +309,9 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
         contract(kt1, kt2, sub * BK);
         const bool full = (key0 + BK <= s.nk) && (!CAUSAL || key0 + BK - 1 <= qw0);
         if (full)
-          fwd_tile_update<CAUSAL, false>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+          fwd_tile_update<RB, CAUSAL, false>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
         else
-          fwd_tile_update<CAUSAL, true>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+          fwd_tile_update<RB, CAUSAL, true>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
       }
     }
     if (st + 1 < nstages) {
@@ -361,7 +360,8 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
 constexpr int kBwdWaves = 8;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdBlocksPerCU = 8 / kBwdWaves;  // 2 waves per SIMD
-constexpr int kBT = 32;              // streamed rows per tile
+constexpr int kBwdRB = 1;                // 32-row blocks per streamed tile
+constexpr int kBT = 32 * kBwdRB;         // streamed rows per tile
 constexpr int kTPitch = kBT + 8;     // pitch (elements) of a transposed tile
 
 __device__ __forceinline__ int tpos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
@@ -517,41 +517,55 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
     const int key0 = t * kBT;
     const bool skip = !wave_live || (CAUSAL && key0 > qw0 + 31);
     if (!skip) {
-      bf16x8 a1[KS], a2[KS];
+      // S^T for the tile's kBwdRB key blocks: 2 * kBwdRB independent accumulation chains
+      f32x16 x1[kBwdRB], x2[kBwdRB];
+#pragma unroll
+      for (int rb = 0; rb < kBwdRB; ++rb) {
+        x1[rb] = f32x16{};
+        x2[rb] = f32x16{};
+      }
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        a1[kk] = lds_a_frag<D>(kt1, col, kk, h);
-        if (!SHARED_K) a2[kk] = lds_a_frag<D>(kt2, col, kk, h);
-      }
-      f32x16 x1 = {}, x2 = {};
+        bf16x8 a1[kBwdRB], a2[kBwdRB];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        x1 = mfma(a1[kk], f1[kk], x1);
-        x2 = mfma(SHARED_K ? a1[kk] : a2[kk], f2[kk], x2);
-      }
-      const bool full = (key0 + kBT <= s.nk) && (!CAUSAL || key0 + kBT - 1 <= qw0);
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e1 = x1[r], e2 = x2[r];
-        const float d12 = e1 - e2;
-        if (!full) {
-          const int key = key0 + acc_row(r, h);
-          const bool ok = key < s.nk && (!CAUSAL || key <= query);
-          e1 = ok ? e1 : -kInf;
-          e2 = ok ? e2 : -kInf;
+        for (int rb = 0; rb < kBwdRB; ++rb) {
+          a1[rb] = lds_a_frag<D>(kt1, rb * 32 + col, kk, h);
+          if (!SHARED_K) a2[rb] = lds_a_frag<D>(kt2, rb * 32 + col, kk, h);
         }
-        const float p1 = exp2_hw(fmaf(e1, c, b1));
-        if (SETTING == 1)
-          ds[r] = exp2_hw(fmaf(e2, c, b2)) - p1;
-        else
-          ds[r] = p1 * fmaf(d12, s.scale, cst);
+#pragma unroll
+        for (int rb = 0; rb < kBwdRB; ++rb) {
+          x1[rb] = mfma(a1[rb], f1[kk], x1[rb]);
+          x2[rb] = mfma(SHARED_K ? a1[rb] : a2[rb], f2[kk], x2[rb]);
+        }
       }
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const bf16x8 a = pack8(ds + 8 * cc);
+      for (int rb = 0; rb < kBwdRB; ++rb) {
+        const int kb0 = key0 + rb * 32;
+        const bool full = (kb0 + 32 <= s.nk) && (!CAUSAL || kb0 + 31 <= qw0);
+        float ds[16];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) dq[nb] = mfma(a, tr_frag(ktr, nb, cc, col, h), dq[nb]);
+        for (int r = 0; r < 16; ++r) {
+          float e1 = x1[rb][r], e2 = x2[rb][r];
+          const float d12 = e1 - e2;
+          if (!full) {
+            const int key = kb0 + acc_row(r, h);
+            const bool ok = key < s.nk && (!CAUSAL || key <= query);
+            e1 = ok ? e1 : -kInf;
+            e2 = ok ? e2 : -kInf;
+          }
+          const float p1 = exp2_hw(fmaf(e1, c, b1));
+          if (SETTING == 1)
+            ds[r] = exp2_hw(fmaf(e2, c, b2)) - p1;
+          else
+            ds[r] = p1 * fmaf(d12, s.scale, cst);
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const bf16x8 a = pack8(ds + 8 * cc);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            dq[nb] = mfma(a, tr_frag(ktr, nb, rb * 2 + cc, col, h), dq[nb]);
+        }
       }
     }
     if (t + 1 < ntiles) {
@@ -664,53 +678,66 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
     const int qt0 = t * kBT;
     const bool skip = !wave_live || (CAUSAL && qt0 + kBT - 1 < kw0);
     if (!skip) {
-      bf16x8 a1[KS], a2[KS];
+      f32x16 x1[kBwdRB], x2[kBwdRB];
+#pragma unroll
+      for (int rb = 0; rb < kBwdRB; ++rb) {
+        x1[rb] = f32x16{};
+        x2[rb] = f32x16{};
+      }
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        a1[kk] = lds_a_frag<D>(qt1, col, kk, h);
-        a2[kk] = lds_a_frag<D>(qt2, col, kk, h);
-      }
-      f32x16 x1 = {}, x2 = {};
+        bf16x8 a1[kBwdRB], a2[kBwdRB];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        x1 = mfma(a1[kk], f1[kk], x1);
-        x2 = mfma(a2[kk], f2[kk], x2);
-      }
-      const bool full = (qt0 + kBT <= s.nq) && (!CAUSAL || qt0 >= kw0 + 31);
-      float ds[16];
+        for (int rb = 0; rb < kBwdRB; ++rb) {
+          a1[rb] = lds_a_frag<D>(qt1, rb * 32 + col, kk, h);
+          a2[rb] = lds_a_frag<D>(qt2, rb * 32 + col, kk, h);
+        }
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        // registers 4rq..4rq+3 hold 4 consecutive queries
-        const int qi = rq * 8 + h * 4;
-        const float4 va0 = *reinterpret_cast<const float4*>(&qa[buf][0][qi]);
-        const float4 va1 = *reinterpret_cast<const float4*>(&qa[buf][1][qi]);
-        const float4 va2 = *reinterpret_cast<const float4*>(&qa[buf][2][qi]);
-        const float c0[4] = {va0.x, va0.y, va0.z, va0.w};
-        const float c1[4] = {va1.x, va1.y, va1.z, va1.w};
-        const float c2[4] = {va2.x, va2.y, va2.z, va2.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = rq * 4 + j;
-          float e1 = x1[r], e2 = x2[r];
-          const float d12 = e1 - e2;
-          if (!full) {
-            const int q = qt0 + qi + j;
-            const bool ok = q < s.nq && (!CAUSAL || key <= q);
-            e1 = ok ? e1 : -kInf;
-            e2 = ok ? e2 : -kInf;
-          }
-          const float p1 = exp2_hw(fmaf(e1, c, c0[j]));
-          if (SETTING == 1)
-            ds[r] = c2[j] * (exp2_hw(fmaf(e2, c, c1[j])) - p1);
-          else
-            ds[r] = c2[j] * (p1 * fmaf(d12, s.scale, c1[j]));
+        for (int rb = 0; rb < kBwdRB; ++rb) {
+          x1[rb] = mfma(a1[rb], f1[kk], x1[rb]);
+          x2[rb] = mfma(a2[rb], f2[kk], x2[rb]);
         }
       }
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const bf16x8 a = pack8(ds + 8 * cc);
+      for (int rb = 0; rb < kBwdRB; ++rb) {
+        const int qb0 = qt0 + rb * 32;
+        const bool full = (qb0 + 32 <= s.nq) && (!CAUSAL || qb0 >= kw0 + 31);
+        float ds[16];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) dk[nb] = mfma(a, tr_frag(qtr, nb, cc, col, h), dk[nb]);
+        for (int rq = 0; rq < 4; ++rq) {
+          // registers 4rq..4rq+3 hold 4 consecutive queries
+          const int qi = rb * 32 + rq * 8 + h * 4;
+          const float4 va0 = *reinterpret_cast<const float4*>(&qa[buf][0][qi]);
+          const float4 va1 = *reinterpret_cast<const float4*>(&qa[buf][1][qi]);
+          const float4 va2 = *reinterpret_cast<const float4*>(&qa[buf][2][qi]);
+          const float c0[4] = {va0.x, va0.y, va0.z, va0.w};
+          const float c1[4] = {va1.x, va1.y, va1.z, va1.w};
+          const float c2[4] = {va2.x, va2.y, va2.z, va2.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = rq * 4 + j;
+            float e1 = x1[rb][r], e2 = x2[rb][r];
+            const float d12 = e1 - e2;
+            if (!full) {
+              const int q = qt0 + qi + j;
+              const bool ok = q < s.nq && (!CAUSAL || key <= q);
+              e1 = ok ? e1 : -kInf;
+              e2 = ok ? e2 : -kInf;
+            }
+            const float p1 = exp2_hw(fmaf(e1, c, c0[j]));
+            if (SETTING == 1)
+              ds[r] = c2[j] * (exp2_hw(fmaf(e2, c, c1[j])) - p1);
+            else
+              ds[r] = c2[j] * (p1 * fmaf(d12, s.scale, c1[j]));
+          }
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const bf16x8 a = pack8(ds + 8 * cc);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            dk[nb] = mfma(a, tr_frag(qtr, nb, rb * 2 + cc, col, h), dk[nb]);
+        }
       }
     }
     if (i + 1 < ntiles) {

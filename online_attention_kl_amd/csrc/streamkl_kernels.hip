@@ -148,13 +148,49 @@ __device__ __forceinline__ void block_coords(int n_slices, int& rank, int& slice
 }
 
 // ================================================================ forward
-// One key tile's contribution to a lane's partial online state. s1 / s2 hold the lane's
-// unscaled dot products of the tile (RB blocks of 32 keys, 16 keys of each block per lane) and
-// are masked in place.
+// Each lane keeps its running state as a running maximum m_t (of the unscaled dot products) and
+// four interleaved partial sums of l1, l2 and acc, all relative to exp2(c * m_t) with
+// c = scale * log2(e): l_t = sum_j exp2(c (x_tj - m_t)), acc = sum_j exp2(c (x1j - m1)) (x1j - x2j).
+//
+// The running maximum is raised only where it must be: on a lane's first tile, and on tiles that
+// take the masked path (the diagonal or the ragged end). Every other tile is accumulated against
+// the current maximum without looking for a new one. That is the same sum up to rounding as long
+// as no exponential overflows (fp32 keeps its relative precision up to 2^127), and it removes the
+// tile maximum, the rescaling and the per-tile reduction from the common path. A lane whose state
+// becomes non-finite, which needs a logit that exceeds every logit of its first tile by more than
+// about 2^7 / c, is recomputed by the exact path at the end of the kernel.
+
+// Adds one tile's exponentials to the partial sums against the current maxima (-c m_t = nb_t).
+// s1 / s2 hold the lane's unscaled dot products of the tile: RB blocks of 32 keys, 16 keys of
+// each block per lane. Masked entries are -inf and contribute 0.
+template <int RB, bool MASK>
+__device__ __forceinline__ void fwd_tile_accumulate(const f32x16 (&s1)[RB], const f32x16 (&s2)[RB],
+                                                    float c, float nb1, float nb2, float (&L1)[4],
+                                                    float (&L2)[4], float (&A)[4]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x1 = s1[rb][r], x2 = s2[rb][r];
+      const float p1 = exp2_hw(fmaf(x1, c, nb1));
+      const float p2 = exp2_hw(fmaf(x2, c, nb2));
+      // masked entries have x1 = x2 = -inf and p1 = 0; their difference must not turn into NaN
+      const float dd = MASK ? (p1 > 0.f ? x1 - x2 : 0.f) : x1 - x2;
+      const int j = r & 3;
+      L1[j] += p1;
+      L2[j] += p2;
+      A[j] = fmaf(p1, dd, A[j]);
+    }
+  }
+}
+
+// One tile with the running maxima raised to the tile's maxima first (the partial sums are
+// rescaled by exp2(c (m_old - m_new))). Applies the causal / ragged-end mask in place when MASK.
 template <int RB, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void fwd_tile_update(f32x16 (&s1)[RB], f32x16 (&s2)[RB], float c,
-                                                int key0, int query, int nk, int h, float& m1,
-                                                float& l1, float& m2, float& l2, float& acc) {
+__device__ __forceinline__ void fwd_tile_exact(f32x16 (&s1)[RB], f32x16 (&s2)[RB], float c,
+                                               int key0, int query, int nk, int h, float& m1,
+                                               float& m2, float& nb1, float& nb2, float (&L1)[4],
+                                               float (&L2)[4], float (&A)[4]) {
   if (MASK) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -166,48 +202,30 @@ __device__ __forceinline__ void fwd_tile_update(f32x16 (&s1)[RB], f32x16 (&s2)[R
         s2[rb][r] = ok ? s2[rb][r] : -kInf;
       }
   }
-  float mx1 = s1[0][0], mx2 = s2[0][0];
+  float mx1 = m1, mx2 = m2;
 #pragma unroll
-  for (int i = 1; i < 16 * RB; i += 2) {
-    const int rb = i / 16, r = i % 16, rb2 = (i + 1) / 16, r2 = (i + 1) % 16;
-    if (i + 1 < 16 * RB) {
-      mx1 = fmaxf(fmaxf(mx1, s1[rb][r]), s1[rb2][r2]);
-      mx2 = fmaxf(fmaxf(mx2, s2[rb][r]), s2[rb2][r2]);
-    } else {
-      mx1 = fmaxf(mx1, s1[rb][r]);
-      mx2 = fmaxf(mx2, s2[rb][r]);
-    }
+  for (int i = 0; i < 16 * RB; i += 2) {
+    const int rb = i / 16, r = i % 16;
+    mx1 = fmaxf(fmaxf(mx1, s1[rb][r]), s1[rb][r + 1]);
+    mx2 = fmaxf(fmaxf(mx2, s2[rb][r]), s2[rb][r + 1]);
   }
-  const float m1n = fmaxf(m1, mx1), m2n = fmaxf(m2, mx2);
-  const float a1 = exp2_hw((m1 - m1n) * c), a2 = exp2_hw((m2 - m2n) * c);
-  const float nb1 = -m1n * c, nb2 = -m2n * c;
-  float sl1[4], sl2[4], sa[4];
+  const float a1 = exp2_hw((m1 - mx1) * c), a2 = exp2_hw((m2 - mx2) * c);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x1 = s1[rb][r], x2 = s2[rb][r];
-      const float p1 = exp2_hw(fmaf(x1, c, nb1));
-      const float p2 = exp2_hw(fmaf(x2, c, nb2));
-      // masked entries have x1 = x2 = -inf and p1 = 0; their difference must not turn into NaN
-      const float dd = MASK ? (p1 > 0.f ? x1 - x2 : 0.f) : x1 - x2;
-      const int j = r & 3;
-      if (rb == 0 && r < 4) {
-        sl1[j] = p1;
-        sl2[j] = p2;
-        sa[j] = p1 * dd;
-      } else {
-        sl1[j] += p1;
-        sl2[j] += p2;
-        sa[j] = fmaf(p1, dd, sa[j]);
-      }
-    }
+  for (int j = 0; j < 4; ++j) {
+    L1[j] *= a1;
+    L2[j] *= a2;
+    A[j] *= a1;
   }
-  l1 = fmaf(l1, a1, (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]));
-  l2 = fmaf(l2, a2, (sl2[0] + sl2[1]) + (sl2[2] + sl2[3]));
-  acc = fmaf(acc, a1, (sa[0] + sa[1]) + (sa[2] + sa[3]));
-  m1 = m1n;
-  m2 = m2n;
+  m1 = mx1;
+  m2 = mx2;
+  nb1 = -mx1 * c;
+  nb2 = -mx2 * c;
+  fwd_tile_accumulate<RB, MASK>(s1, s2, c, nb1, nb2, L1, L2, A);
+}
+
+__device__ __forceinline__ bool non_finite(float x) {
+  // bit test: stays valid when the compiler is told that NaNs do not occur
+  return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u;
 }
 
 // Forward launch shape: blocks of kFwdWaves waves (32 query rows each), kFwdBlocksPerCU blocks
@@ -261,7 +279,8 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   const float c = s.scale * kLog2e;
   const bool wave_live = qw0 < s.nq;
 
-  float m1 = kNegBig, m2 = kNegBig, l1 = 0.f, l2 = 0.f, acc = 0.f;
+  float m1 = kNegBig, m2 = kNegBig, nb1 = 0.f, nb2 = 0.f;
+  float L1[4] = {}, L2[4] = {}, A[4] = {};
   TileRegs<SB, D, kFwdThreads> r1, r2;
   r1.load(K1, s.k_sr, 0, s.nk);
   if (!SHARED_K) r2.load(K2, s.k_sr, 0, s.nk);
@@ -308,10 +327,12 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
       if (t < ntiles && wave_live && !(CAUSAL && key0 > qw0 + 31)) {
         contract(kt1, kt2, sub * BK);
         const bool full = (key0 + BK <= s.nk) && (!CAUSAL || key0 + BK - 1 <= qw0);
-        if (full)
-          fwd_tile_update<RB, CAUSAL, false>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+        if (full && t > 0)
+          fwd_tile_accumulate<RB, false>(s1, s2, c, nb1, nb2, L1, L2, A);
+        else if (full)
+          fwd_tile_exact<RB, CAUSAL, false>(s1, s2, c, key0, query, s.nk, h, m1, m2, nb1, nb2, L1, L2, A);
         else
-          fwd_tile_update<RB, CAUSAL, true>(s1, s2, c, key0, query, s.nk, h, m1, l1, m2, l2, acc);
+          fwd_tile_exact<RB, CAUSAL, true>(s1, s2, c, key0, query, s.nk, h, m1, m2, nb1, nb2, L1, L2, A);
       }
     }
     if (st + 1 < nstages) {
@@ -327,6 +348,39 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
     __syncthreads();
   }
 
+  float l1 = (L1[0] + L1[1]) + (L1[2] + L1[3]);
+  float l2 = (L2[0] + L2[1]) + (L2[2] + L2[3]);
+  float acc = (A[0] + A[1]) + (A[2] + A[3]);
+
+  // Exact path for a wave with an overflowed lane: every tile again, each one raising the
+  // maxima, with the key tiles read straight from global memory (no LDS, no barrier).
+  const bool bad = non_finite(l1) || non_finite(l2) || non_finite(acc);
+  if (wave_live && __any(bad)) {
+    m1 = m2 = kNegBig;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) L1[j] = L2[j] = A[j] = 0.f;
+    const int wend = CAUSAL ? min(kend, qw0 + 32) : kend;
+    for (int key0 = 0; key0 < wend; key0 += 32) {
+      f32x16 x1[1] = {f32x16{}}, x2[1] = {f32x16{}};
+      const int key = key0 + col;
+      const bool kin = key < s.nk;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        bf16x8 a1 = {}, a2 = {};
+        if (kin) {
+          a1 = load_frag(K1 + (long long)key * s.k_sr + kk * 16 + h * 8);
+          a2 = load_frag(K2 + (long long)key * s.k_sr + kk * 16 + h * 8);
+        }
+        x1[0] = mfma(a1, f1[kk], x1[0]);
+        x2[0] = mfma(a2, f2[kk], x2[0]);
+      }
+      fwd_tile_exact<1, CAUSAL, true>(x1, x2, c, key0, query, s.nk, h, m1, m2, nb1, nb2, L1, L2, A);
+    }
+    l1 = (L1[0] + L1[1]) + (L1[2] + L1[3]);
+    l2 = (L2[0] + L2[1]) + (L2[2] + L2[3]);
+    acc = (A[0] + A[1]) + (A[2] + A[3]);
+  }
+
   // Merge the two partial states of this query row (lanes l and l ^ 32).
   const float om1 = __shfl_xor(m1, 32), ol1 = __shfl_xor(l1, 32);
   const float om2 = __shfl_xor(m2, 32), ol2 = __shfl_xor(l2, 32);
@@ -335,13 +389,13 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
     const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
     const float fa = exp2_hw((m1 - M1) * c), fb = exp2_hw((om1 - M1) * c);
     const float ga = exp2_hw((m2 - M2) * c), gb = exp2_hw((om2 - M2) * c);
-    const float L1 = l1 * fa + ol1 * fb;
-    const float L2 = l2 * ga + ol2 * gb;
-    const float A = acc * fa + oacc * fb;
-    const float lse1 = M1 * s.scale + log2_hw(L1) * kLn2;
-    const float lse2 = M2 * s.scale + log2_hw(L2) * kLn2;
+    const float L1s = l1 * fa + ol1 * fb;
+    const float L2s = l2 * ga + ol2 * gb;
+    const float As = acc * fa + oacc * fb;
+    const float lse1 = M1 * s.scale + log2_hw(L1s) * kLn2;
+    const float lse2 = M2 * s.scale + log2_hw(L2s) * kLn2;
     const long long o = (long long)slice * s.nq + query;
-    kl_out[o] = s.scale * A / L1 + (lse2 - lse1);
+    kl_out[o] = s.scale * As / L1s + (lse2 - lse1);
     lse1_out[o] = lse1;
     lse2_out[o] = lse2;
   }

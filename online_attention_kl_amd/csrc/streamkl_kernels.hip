@@ -39,6 +39,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <string>
+#include <type_traits>
 
 #include "../../include/streamkl.h"
 
@@ -592,16 +593,17 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           x2[rb] = mfma(SHARED_K ? a1[rb] : a2[rb], f2[kk], x2[rb]);
         }
       }
-#pragma unroll
-      for (int rb = 0; rb < kBwdRB; ++rb) {
+      // dS of one 32-key block and its dQ product; the element mask is compiled only into the
+      // variant used on tiles that straddle the diagonal or the ragged end
+      auto ds_block = [&](auto maskc, int rb) {
+        constexpr bool MASK = decltype(maskc)::value;
         const int kb0 = key0 + rb * 32;
-        const bool full = (kb0 + 32 <= s.nk) && (!CAUSAL || kb0 + 31 <= qw0);
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float e1 = x1[rb][r], e2 = x2[rb][r];
           const float d12 = e1 - e2;
-          if (!full) {
+          if (MASK) {
             const int key = kb0 + acc_row(r, h);
             const bool ok = key < s.nk && (!CAUSAL || key <= query);
             e1 = ok ? e1 : -kInf;
@@ -620,6 +622,14 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           for (int nb = 0; nb < NB; ++nb)
             dq[nb] = mfma(a, tr_frag(ktr, nb, rb * 2 + cc, col, h), dq[nb]);
         }
+      };
+#pragma unroll
+      for (int rb = 0; rb < kBwdRB; ++rb) {
+        const int kb0 = key0 + rb * 32;
+        if ((kb0 + 32 <= s.nk) && (!CAUSAL || kb0 + 31 <= qw0))
+          ds_block(std::false_type{}, rb);
+        else
+          ds_block(std::true_type{}, rb);
       }
     }
     if (t + 1 < ntiles) {
@@ -752,10 +762,10 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           x2[rb] = mfma(a2[rb], f2[kk], x2[rb]);
         }
       }
-#pragma unroll
-      for (int rb = 0; rb < kBwdRB; ++rb) {
-        const int qb0 = qt0 + rb * 32;
-        const bool full = (qb0 + 32 <= s.nq) && (!CAUSAL || qb0 >= kw0 + 31);
+      // dS^T of one 32-query block and its dK product; the element mask is compiled only into
+      // the variant used on tiles that straddle the diagonal or the ragged end
+      auto ds_block = [&](auto maskc, int rb) {
+        constexpr bool MASK = decltype(maskc)::value;
         float ds[16];
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
@@ -772,7 +782,7 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
             const int r = rq * 4 + j;
             float e1 = x1[rb][r], e2 = x2[rb][r];
             const float d12 = e1 - e2;
-            if (!full) {
+            if (MASK) {
               const int q = qt0 + qi + j;
               const bool ok = q < s.nq && (!CAUSAL || key <= q);
               e1 = ok ? e1 : -kInf;
@@ -792,6 +802,14 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           for (int nb = 0; nb < NB; ++nb)
             dk[nb] = mfma(a, tr_frag(qtr, nb, rb * 2 + cc, col, h), dk[nb]);
         }
+      };
+#pragma unroll
+      for (int rb = 0; rb < kBwdRB; ++rb) {
+        const int qb0 = qt0 + rb * 32;
+        if ((qb0 + 32 <= s.nq) && (!CAUSAL || qb0 >= kw0 + 31))
+          ds_block(std::false_type{}, rb);
+        else
+          ds_block(std::true_type{}, rb);
       }
     }
     if (i + 1 < ntiles) {

@@ -56,6 +56,57 @@ def traffic_for(kernel: str, workload: str):
     return k["fetch_bytes"] + k["write_bytes"]
 
 
+def write_traffic(fetch_dir: str, write_dir: str, workload: str) -> dict:
+    """Per-launch HBM bytes from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch) of `bench.py --copy-calibration`, scaled by what the same counters read for the
+    plain 1 GiB device copy that run starts with; written to profiles/hbm_traffic.json together
+    with the SHA-256 of the kernel source they describe."""
+    import csv
+    import glob
+    import re
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals, copy = {}, []
+        for r in csv.DictReader(open(files[0])):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0
+            if "copyBuffer" in name:
+                copy.append(v)
+                continue
+            m = re.search(r"(fwd|dq|dk)_kernel(?:ILi\d+ELi(\d)E)?", name)
+            if m:
+                key = m.group(1) + "_kernel" + (f"_s{m.group(2)}" if m.group(2) else "")
+                vals.setdefault(key, []).append(v)
+        if not copy:
+            raise SystemExit(f"{d}: no calibration copy found (run bench.py --copy-calibration)")
+        return {k: sum(v) / len(v) for k, v in vals.items()}, copy[0]
+
+    gib = float(1 << 30)
+    fetch, fcopy = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, wcopy = per_kernel(write_dir, "WRITE_SIZE")
+    fs, ws = gib / fcopy, gib / wcopy
+    out = {
+        "workload": workload,
+        "source_sha256": source_sha(),
+        "command": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> -T "
+                   "-f csv -d <repo>/gpurun_out/traffic_<C> -o run -- python3 <repo>/bench.py "
+                   "--steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
+        "copy_reference": {"bytes_read": int(gib), "bytes_written": int(gib),
+                           "fetch_counter_bytes": fcopy, "write_counter_bytes": wcopy,
+                           "fetch_scale": fs, "write_scale": ws},
+        "kernels": {k: {"fetch_bytes": fetch[k] * fs, "write_bytes": write.get(k, 0.0) * ws}
+                    for k in sorted(fetch)},
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 def cpu_baseline(w, x, target_s: float):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload: blocks of 256
     query rows spread evenly over the row range of several slices, forward plus the workload's
@@ -119,7 +170,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device copy of 1 GiB (reference for HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 counter runs into profiles/hbm_traffic.json "
+                         "(no GPU work)")
     args = ap.parse_args()
+    if args.write_traffic:
+        print(json.dumps(write_traffic(*args.write_traffic, args.workload), indent=1))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the StreamKL path here runs on a single MI355X "
               "(slices would shard across GPUs with no communication; not built). "

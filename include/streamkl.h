@@ -65,8 +65,13 @@ typedef struct {
  *
  * Streams key tiles through on-chip memory and keeps per query row the running maxima m1, m2,
  * the running sums of exponentials l1, l2 and the P1-weighted logit-difference accumulator acc,
- * rescaled whenever a running maximum grows; then writes
+ * all relative to the running maxima; then writes
  *     lse_t[i] = m_t + log l_t,      kl[i] = acc / l1 + lse2[i] - lse1[i].
+ * The running maxima are raised on a row's first key tile and on tiles that need the causal or
+ * ragged-end mask; other tiles are summed against the current maxima (the same sums up to
+ * rounding). A row whose sums would leave the float32 range that way (a logit exceeding every
+ * logit of its first tile by more than about 88 / (scale * log2(e)) in unscaled units, i.e.
+ * 2^7 in exp2 units) is recomputed with the maxima raised on every tile.
  * Outputs (device, float32, contiguous [batch, heads, n_q], overwritten): kl, lse1, lse2.
  * The result is bitwise deterministic, and kl is exactly 0 where (Q1, K1) and (Q2, K2) hold
  * identical values.
@@ -74,6 +79,43 @@ typedef struct {
 streamkl_status_t streamkl_fwd(const streamkl_problem_t* problem,
                                const void* q1, const void* k1, const void* q2, const void* k2,
                                float* kl, float* lse1, float* lse2, hipStream_t stream);
+
+/*
+ * Split-K forward for few query rows (gist.science/pt "Resumo Tecnico", section "3. Otimizacoes
+ * de Kernel de GPU", Split-K variant; its gain for small N_Q under "Resultados Experimentais",
+ * ablation). Same outputs and semantics as streamkl_fwd, for any sizes.
+ *
+ * The keys of every slice are cut into n_splits contiguous ranges of whole 32-key tiles. Each
+ * (slice, 32-row query block, range) is one independent work item of one wavefront, which
+ * writes the partial online state (m1, l1, m2, l2, acc) of its rows to the workspace; a second
+ * kernel merges the ranges of each row (the online state of a union of key sets follows from
+ * the states of its parts: the larger maximum wins and the other sums are rescaled) and writes
+ * kl, lse1, lse2. Results agree with streamkl_fwd to float32 rounding (summation order differs)
+ * and are bitwise deterministic for a given n_splits.
+ *
+ * n_splits: requested number of ranges; <= 0 chooses streamkl_fwd_splitk_default_splits().
+ *   The number used is min(n_splits, number of key tiles, 4096), then reduced so that no range
+ *   is empty.
+ * workspace: device memory of at least streamkl_fwd_splitk_workspace_size(problem, n_splits)
+ *   bytes, 16-byte aligned, owned by the caller, not overlapping any input or output; its
+ *   contents on entry are ignored and on return are unspecified. It holds float32
+ *   [batch * heads][ranges used][5][n_q].
+ * Errors: as streamkl_fwd, plus STREAMKL_ERROR_INVALID_VALUE for a NULL, misaligned,
+ *   overlapping or too small workspace.
+ */
+/* Number of key ranges chosen for n_splits <= 0: about 4096 work items with at least 8 key
+ * tiles per range (only tiles some row can see count when causal); 1 when there are more than
+ * 256 work items without splitting, where streamkl_fwd is the faster path. 0 for a NULL problem
+ * or sizes < 1. */
+int32_t streamkl_fwd_splitk_default_splits(const streamkl_problem_t* problem);
+/* Workspace bytes streamkl_fwd_splitk needs for this n_splits; 0 for a NULL problem or sizes
+ * < 1. */
+size_t streamkl_fwd_splitk_workspace_size(const streamkl_problem_t* problem, int32_t n_splits);
+streamkl_status_t streamkl_fwd_splitk(const streamkl_problem_t* problem,
+                                      const void* q1, const void* k1, const void* q2,
+                                      const void* k2, float* kl, float* lse1, float* lse2,
+                                      int32_t n_splits, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /*
  * Backward, setting 1: P1 fixed (stop-gradient), P2 free - standard distillation

@@ -7,6 +7,8 @@ HIP kernels; there is no fallback. If the library has not been built, `lib()` ra
 
 Functions (names follow the C ABI):
   streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False)           -> (kl, lse1, lse2)
+  streamkl_fwd_splitk(q1, k1, q2, k2, n_splits=0, ...)             -> (kl, lse1, lse2)
+  streamkl_fwd_splitk_default_splits(q1, k1, ...), streamkl_fwd_splitk_workspace_size(...)
   streamkl_bwd_fixP1(q1, k1, q2, k2, lse1, lse2, grad_kl, ...)      -> (dq2, dk2)
   streamkl_bwd_fixP2(q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...)  -> (dq1, dk1)
   streamkl_bwd_dq(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...) -> dq (one kernel)
@@ -25,8 +27,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamkl
 STATUS = {0: "STREAMKL_SUCCESS", 1: "STREAMKL_ERROR_INVALID_VALUE",
           2: "STREAMKL_ERROR_NOT_SUPPORTED", 3: "STREAMKL_ERROR_HIP"}
 
-EXPORTS = ("streamkl_fwd", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2", "streamkl_bwd_dq",
-           "streamkl_bwd_dk", "streamkl_status_string", "streamkl_last_error")
+EXPORTS = ("streamkl_fwd", "streamkl_fwd_splitk", "streamkl_fwd_splitk_default_splits",
+           "streamkl_fwd_splitk_workspace_size", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2",
+           "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_status_string",
+           "streamkl_last_error")
 
 
 class StreamKLError(RuntimeError):
@@ -58,6 +62,13 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     vp, fp = ctypes.c_void_p, ctypes.c_void_p
     pp = ctypes.POINTER(Problem)
     L.streamkl_fwd.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp]
+    L.streamkl_fwd_splitk.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, ctypes.c_int32, vp,
+                                      ctypes.c_size_t, vp]
+    L.streamkl_fwd_splitk.restype = ctypes.c_int
+    L.streamkl_fwd_splitk_default_splits.argtypes = [pp]
+    L.streamkl_fwd_splitk_default_splits.restype = ctypes.c_int32
+    L.streamkl_fwd_splitk_workspace_size.argtypes = [pp, ctypes.c_int32]
+    L.streamkl_fwd_splitk_workspace_size.restype = ctypes.c_size_t
     L.streamkl_bwd_fixP1.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp, vp, vp]
     L.streamkl_bwd_fixP2.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, fp, vp, vp, vp]
     for name in ("streamkl_bwd_dq", "streamkl_bwd_dk"):
@@ -133,6 +144,43 @@ def streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False, out=None):
     _check(lib().streamkl_fwd(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
                               k2.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
                               out[2].data_ptr(), _stream(q1)))
+    return out
+
+
+def streamkl_fwd_splitk_default_splits(q1, k1, scale=None, causal=False) -> int:
+    p = make_problem(q1, k1, scale, causal)
+    return int(lib().streamkl_fwd_splitk_default_splits(ctypes.byref(p)))
+
+
+def streamkl_fwd_splitk_workspace_size(q1, k1, n_splits=0, scale=None, causal=False) -> int:
+    p = make_problem(q1, k1, scale, causal)
+    return int(lib().streamkl_fwd_splitk_workspace_size(ctypes.byref(p), int(n_splits)))
+
+
+def streamkl_fwd_splitk(q1, k1, q2, k2, scale=None, causal=False, n_splits=0, workspace=None,
+                        out=None):
+    """Split-K forward for few query rows: the same (kl, lse1, lse2) as streamkl_fwd. The
+    workspace (a uint8 CUDA tensor of at least streamkl_fwd_splitk_workspace_size bytes) is
+    allocated here when not given."""
+    import torch
+    _check_inputs(q1, k1, q2, k2)
+    B, H, nq, _ = q1.shape
+    if out is None:
+        out = tuple(torch.empty((B, H, nq), dtype=torch.float32, device=q1.device)
+                    for _ in range(3))
+    for n, t in zip(("kl", "lse1", "lse2"), out):
+        _rowvec(t, n, (B, H, nq))
+    p = make_problem(q1, k1, scale, causal)
+    need = int(lib().streamkl_fwd_splitk_workspace_size(ctypes.byref(p), int(n_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().streamkl_fwd_splitk(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(),
+                                     q2.data_ptr(), k2.data_ptr(), out[0].data_ptr(),
+                                     out[1].data_ptr(), out[2].data_ptr(), int(n_splits),
+                                     workspace.data_ptr(), nbytes, _stream(q1)))
     return out
 
 

@@ -402,6 +402,144 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   }
 }
 
+// ================================================================ split-K forward
+// With few query rows (decode-like shapes) one block per 256-row query block leaves most of the
+// chip idle. Here every wave has its own work item: a 32-row query block of one slice and one
+// contiguous range of key tiles. The wave reads its keys straight from global memory into MFMA
+// operands (no LDS and no barrier: no other wave of the block reads the same keys), runs the
+// forward's online update and writes the partial state of each row (m1, l1, m2, l2, acc; l and
+// acc relative to exp2(c m)) to a workspace laid out [slice][range][5][n_q]. A second kernel
+// merges the ranges of each row (merging two online states is associative: the larger maximum
+// wins and the other sums are rescaled by exp2(c (m_a - m))) and finishes KL, LSE1 and LSE2.
+constexpr int kSplitWaves = 4;  // independent work items per block
+
+template <int D, bool CAUSAL, bool SHARED_K>
+__global__ void __launch_bounds__(64 * kSplitWaves)
+fwd_split_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
+                 const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
+                 float* __restrict__ part, Shape s, int nsplit, int split_keys) {
+  constexpr int KS = D / 16;
+  const int nqb = (s.nq + 31) / 32;
+  const long long item = (long long)blockIdx.x * kSplitWaves + wave_id();
+  if (item >= (long long)s.bh * nqb * nsplit) return;  // nothing below synchronises the block
+  const int split = (int)(item % nsplit);
+  const long long rest = item / nsplit;
+  const int qb = (int)(rest % nqb), slice = (int)(rest / nqb);
+  const int b = slice / s.heads, hd = slice - b * s.heads;
+  const uint16_t* Q1 = q1 + b * s.q_sb + hd * s.q_sh;
+  const uint16_t* Q2 = q2 + b * s.q_sb + hd * s.q_sh;
+  const uint16_t* K1 = k1 + b * s.k_sb + hd * s.k_sh;
+  const uint16_t* K2 = k2 + b * s.k_sb + hd * s.k_sh;
+
+  const int l = lane_id(), h = l >> 5, col = l & 31;
+  const int q0 = qb * 32;
+  const int query = q0 + col;
+  const int qrow = query < s.nq ? query : s.nq - 1;
+  bf16x8 f1[KS], f2[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    f1[kk] = load_frag(Q1 + (long long)qrow * s.q_sr + kk * 16 + h * 8);
+    f2[kk] = load_frag(Q2 + (long long)qrow * s.q_sr + kk * 16 + h * 8);
+  }
+  const int kbeg = split * split_keys;
+  int kend = min(s.nk, kbeg + split_keys);
+  if (CAUSAL) kend = min(kend, min(s.nq - 1, q0 + 31) + 1);
+  const float c = s.scale * kLog2e;
+
+  float m1, m2, nb1, nb2, L1[4], L2[4], A[4];
+  f32x16 x1[1], x2[1];
+  // pass 0 raises the maxima only on the range's first tile and on masked tiles; a wave with a
+  // lane whose state overflowed repeats its range with every tile raising them (pass 1)
+  for (int pass = 0; pass < 2; ++pass) {
+    m1 = m2 = kNegBig;
+    nb1 = nb2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) L1[j] = L2[j] = A[j] = 0.f;
+    // operands of the next tile are loaded while the current one is contracted and updated;
+    // rows past n_k are read clamped and masked by the exact update
+    bf16x8 a1[KS], a2[KS];
+    auto fetch = [&](int key0) {
+      const long long ro = (long long)min(key0 + col, s.nk - 1) * s.k_sr + h * 8;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        a1[kk] = load_frag(K1 + ro + kk * 16);
+        if (!SHARED_K) a2[kk] = load_frag(K2 + ro + kk * 16);
+      }
+    };
+    if (kbeg < kend) fetch(kbeg);
+    for (int key0 = kbeg; key0 < kend; key0 += 32) {
+      x1[0] = f32x16{};
+      x2[0] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        x1[0] = mfma(a1[kk], f1[kk], x1[0]);
+        x2[0] = mfma(SHARED_K ? a1[kk] : a2[kk], f2[kk], x2[0]);
+      }
+      if (key0 + 32 < kend) fetch(key0 + 32);
+      const bool full = (key0 + 32 <= s.nk) && (!CAUSAL || key0 + 31 <= q0);
+      if (pass == 0 && full && key0 > kbeg)
+        fwd_tile_accumulate<1, false>(x1, x2, c, nb1, nb2, L1, L2, A);
+      else if (full)
+        fwd_tile_exact<1, CAUSAL, false>(x1, x2, c, key0, query, s.nk, h, m1, m2, nb1, nb2, L1,
+                                         L2, A);
+      else
+        fwd_tile_exact<1, CAUSAL, true>(x1, x2, c, key0, query, s.nk, h, m1, m2, nb1, nb2, L1,
+                                        L2, A);
+    }
+    const bool bad = non_finite((L1[0] + L1[1]) + (L1[2] + L1[3])) ||
+                     non_finite((L2[0] + L2[1]) + (L2[2] + L2[3])) ||
+                     non_finite((A[0] + A[1]) + (A[2] + A[3]));
+    if (!__any(bad)) break;
+  }
+  float l1 = (L1[0] + L1[1]) + (L1[2] + L1[3]);
+  float l2 = (L2[0] + L2[1]) + (L2[2] + L2[3]);
+  float acc = (A[0] + A[1]) + (A[2] + A[3]);
+  // merge the two halves of each row (lanes l and l ^ 32)
+  const float om1 = __shfl_xor(m1, 32), ol1 = __shfl_xor(l1, 32);
+  const float om2 = __shfl_xor(m2, 32), ol2 = __shfl_xor(l2, 32);
+  const float oacc = __shfl_xor(acc, 32);
+  if (h == 0 && query < s.nq) {
+    const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
+    const float fa = exp2_hw((m1 - M1) * c), fb = exp2_hw((om1 - M1) * c);
+    const float ga = exp2_hw((m2 - M2) * c), gb = exp2_hw((om2 - M2) * c);
+    float* o = part + ((long long)slice * nsplit + split) * 5 * s.nq + query;
+    o[0] = M1;
+    o[s.nq] = l1 * fa + ol1 * fb;
+    o[2 * s.nq] = M2;
+    o[3 * s.nq] = l2 * ga + ol2 * gb;
+    o[4 * s.nq] = acc * fa + oacc * fb;
+  }
+}
+
+// One thread per (slice, query row): merge the nsplit partial states and finish the row.
+__global__ void __launch_bounds__(256)
+fwd_merge_kernel(const float* __restrict__ part, float* __restrict__ kl_out,
+                 float* __restrict__ lse1_out, float* __restrict__ lse2_out, Shape s, int nsplit) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)s.bh * s.nq) return;
+  const int slice = (int)(idx / s.nq), q = (int)(idx - (long long)slice * s.nq);
+  const float c = s.scale * kLog2e;
+  const float* p = part + (long long)slice * nsplit * 5 * s.nq + q;
+  float M1 = kNegBig, M2 = kNegBig;
+  for (int i = 0; i < nsplit; ++i) {
+    M1 = fmaxf(M1, p[(long long)(5 * i) * s.nq]);
+    M2 = fmaxf(M2, p[(long long)(5 * i + 2) * s.nq]);
+  }
+  float L1 = 0.f, L2 = 0.f, A = 0.f;
+  for (int i = 0; i < nsplit; ++i) {
+    const float* pi = p + (long long)(5 * i) * s.nq;
+    const float e1 = exp2_hw((pi[0] - M1) * c), e2 = exp2_hw((pi[2 * s.nq] - M2) * c);
+    L1 = fmaf(pi[s.nq], e1, L1);
+    A = fmaf(pi[4 * s.nq], e1, A);
+    L2 = fmaf(pi[3 * s.nq], e2, L2);
+  }
+  const float lse1 = M1 * s.scale + log2_hw(L1) * kLn2;
+  const float lse2 = M2 * s.scale + log2_hw(L2) * kLn2;
+  kl_out[idx] = s.scale * A / L1 + (lse2 - lse1);
+  lse1_out[idx] = lse1;
+  lse2_out[idx] = lse2;
+}
+
 // ================================================================ backward
 // Both backward kernels stream 32-row tiles of the "other" side (key rows for the dQ kernel,
 // query rows for the dK kernel) through double-buffered LDS, one barrier per tile, with 8 waves
@@ -931,6 +1069,55 @@ void launch_fwd(const Shape& s, const void* q1, const void* k1, const void* q2, 
                      (const uint16_t*)k2, kl, l1, l2, s);
 }
 
+// Key ranges of the split-K forward: n_splits requested (<= 0: chosen here) -> tiles per range
+// and the number of ranges actually used (no range is empty of tiles).
+struct SplitPlan {
+  int nsplit, split_keys;
+};
+
+SplitPlan split_plan(const streamkl_problem_t* p, int32_t n_splits) {
+  // with the top-left causal mask no row sees a key past n_q - 1
+  const int64_t nvis = p->causal && p->n_q < p->n_k ? p->n_q : p->n_k;
+  const int64_t ntiles = (nvis + 31) / 32;
+  const int64_t items = p->batch * p->heads * ((p->n_q + 31) / 32);
+  int64_t ns = n_splits;
+  if (ns <= 0) {
+    if (items > 256) {
+      ns = 1;  // one work item per CU or more already: the one-pass forward is the better path
+    } else {
+      // about 4096 waves in flight (16 per CU), at least 8 key tiles per range
+      ns = (4096 + items - 1) / items;
+      const int64_t cap = (ntiles + 7) / 8;
+      if (ns > cap) ns = cap;
+    }
+  }
+  if (ns > ntiles) ns = ntiles;
+  if (ns > 4096) ns = 4096;
+  if (ns < 1) ns = 1;
+  const int64_t tiles_per = (ntiles + ns - 1) / ns;
+  const int64_t used = (ntiles + tiles_per - 1) / tiles_per;
+  return {(int)used, (int)(tiles_per * 32)};
+}
+
+size_t split_workspace_bytes(const streamkl_problem_t* p, int nsplit) {
+  return (size_t)p->batch * p->heads * p->n_q * nsplit * 5 * sizeof(float);
+}
+
+template <int D, bool CAUSAL, bool SK>
+void launch_fwd_split(const Shape& s, const SplitPlan& plan, const void* q1, const void* k1,
+                      const void* q2, const void* k2, float* part, float* kl, float* l1,
+                      float* l2, hipStream_t st) {
+  const long long items = (long long)s.bh * ((s.nq + 31) / 32) * plan.nsplit;
+  const long long blocks = (items + kSplitWaves - 1) / kSplitWaves;
+  hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL, SK>), dim3((unsigned)blocks),
+                     dim3(64 * kSplitWaves), 0, st, (const uint16_t*)q1, (const uint16_t*)k1,
+                     (const uint16_t*)q2, (const uint16_t*)k2, part, s, plan.nsplit,
+                     plan.split_keys);
+  const long long rows = (long long)s.bh * s.nq;
+  hipLaunchKernelGGL(fwd_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
+                     (const float*)part, kl, l1, l2, s, plan.nsplit);
+}
+
 template <int D, int SET, bool CAUSAL, bool SK>
 void launch_bwd(const Shape& s, const void* q1, const void* k1, const void* q2, const void* k2,
                 const float* l1, const float* l2, const float* kl, const float* g, void* dq,
@@ -1024,6 +1211,54 @@ streamkl_status_t streamkl_fwd(const streamkl_problem_t* p, const void* q1, cons
   }
 #undef SKL_FWD
   return check_launch("streamkl_fwd");
+}
+
+int32_t streamkl_fwd_splitk_default_splits(const streamkl_problem_t* p) {
+  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1) return 0;
+  return split_plan(p, 0).nsplit;
+}
+
+size_t streamkl_fwd_splitk_workspace_size(const streamkl_problem_t* p, int32_t n_splits) {
+  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1) return 0;
+  return split_workspace_bytes(p, split_plan(p, n_splits).nsplit);
+}
+
+streamkl_status_t streamkl_fwd_splitk(const streamkl_problem_t* p, const void* q1,
+                                      const void* k1, const void* q2, const void* k2, float* kl,
+                                      float* lse1, float* lse2, int32_t n_splits,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  Shape s;
+  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
+  if (st != STREAMKL_SUCCESS) return st;
+  const SplitPlan plan = split_plan(p, n_splits);
+  const size_t need = split_workspace_bytes(p, plan.nsplit);
+  if (workspace_bytes < need)
+    return fail(STREAMKL_ERROR_INVALID_VALUE,
+                "streamkl_fwd_splitk: workspace too small (" + std::to_string(workspace_bytes) +
+                    " < " + std::to_string(need) + " bytes)");
+  const int64_t n = p->batch * p->heads * p->n_q;
+  const Span outs[4] = {flat_span(kl, n, 4), flat_span(lse1, n, 4), flat_span(lse2, n, 4),
+                        {reinterpret_cast<uintptr_t>(workspace),
+                         reinterpret_cast<uintptr_t>(workspace) + need}};
+  st = check_outputs(p, q1, k1, q2, k2, outs, 4, "streamkl_fwd_splitk");
+  if (st != STREAMKL_SUCCESS) return st;
+  if ((long long)s.bh * ((s.nq + 31) / 32) * plan.nsplit / kSplitWaves >= (1LL << 31))
+    return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_fwd_splitk: grid too large");
+  (void)hipGetLastError();
+  const bool sk = k1 == k2, causal = p->causal != 0;
+  float* part = static_cast<float*>(workspace);
+#define SKL_FWDS(DD, C, S) \
+  launch_fwd_split<DD, C, S>(s, plan, q1, k1, q2, k2, part, kl, lse1, lse2, stream)
+  if (p->head_dim == 64) {
+    if (causal) { if (sk) SKL_FWDS(64, true, true); else SKL_FWDS(64, true, false); }
+    else { if (sk) SKL_FWDS(64, false, true); else SKL_FWDS(64, false, false); }
+  } else {
+    if (causal) { if (sk) SKL_FWDS(128, true, true); else SKL_FWDS(128, true, false); }
+    else { if (sk) SKL_FWDS(128, false, true); else SKL_FWDS(128, false, false); }
+  }
+#undef SKL_FWDS
+  return check_launch("streamkl_fwd_splitk");
 }
 
 streamkl_status_t streamkl_bwd_fixP1(const streamkl_problem_t* p, const void* q1,

@@ -107,3 +107,43 @@ def test_invalid_pointers():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         skl.lib(str(tmp_path / "nope.so"))
+
+
+def splitk(p, ws, nbytes, n_splits=0, o=(O1, O2, O3)):
+    return skl.lib().streamkl_fwd_splitk(ctypes.byref(p), Q1, K1, Q2, K2, *o, n_splits, ws,
+                                         nbytes, None)
+
+
+def test_splitk_plan_and_workspace_size():
+    L = skl.lib()
+    assert L.streamkl_fwd_splitk_default_splits(None) == 0
+    assert L.streamkl_fwd_splitk_workspace_size(None, 4) == 0
+    for nq, nk in ((1, 65536), (16, 4096), (64, 80), (300, 33), (7, 1)):
+        p = good_problem()
+        p.n_q, p.n_k = nq, nk
+        ntiles = (nk + 31) // 32
+        per_range = 2 * nq * 5 * 4  # batch * heads * n_q * 5 floats
+        d = L.streamkl_fwd_splitk_default_splits(ctypes.byref(p))
+        assert 1 <= d <= ntiles
+        # the default keeps at least 8 key tiles per range unless there are fewer tiles
+        assert d == 1 or -(-ntiles // d) >= 8
+        assert L.streamkl_fwd_splitk_workspace_size(ctypes.byref(p), 0) == d * per_range
+        for req in (1, 2, 3, 5, 64, 10 ** 6):
+            used = L.streamkl_fwd_splitk_workspace_size(ctypes.byref(p), req) // per_range
+            assert 1 <= used <= min(req, ntiles, 4096)
+            tiles_per = -(-ntiles // used)
+            assert -(-ntiles // tiles_per) == used  # no range is empty
+            # as many ranges as the request allows, up to ceil(ntiles / ceil(ntiles / req))
+            r = min(req, ntiles, 4096)
+            assert used == -(-ntiles // -(-ntiles // r))
+
+
+def test_splitk_invalid_workspace():
+    p = good_problem()
+    need = skl.lib().streamkl_fwd_splitk_workspace_size(ctypes.byref(p), 1)
+    WS = 0x7A000000
+    assert splitk(p, 0, need, 1) == 1
+    assert splitk(p, WS, need - 4, 1) == 1 and "workspace too small" in last_error()
+    assert splitk(p, WS + 8, need, 1) == 1 and "aligned" in last_error()
+    assert splitk(p, Q1 + 64, need, 1) == 1 and "overlap" in last_error()
+    assert splitk(p, WS, need, 1, o=(O1, WS + 16, O3)) == 1

@@ -172,6 +172,41 @@ streamkl_status_t streamkl_bwd_dk(const streamkl_problem_t* problem, int32_t set
                                   const float* lse1, const float* lse2, const float* kl,
                                   const float* grad_kl, void* dk, hipStream_t stream);
 
+/*
+ * dQ with the keys split into ranges, for few query rows: the adaptive side of the backward
+ * (gist.science/pt "Resumo Tecnico": "Metodologia" section 2, kernel fusion and the conflict
+ * between accumulating dQ along K and dK along Q; "Resultados Experimentais", ablation: the
+ * kernel choice adapts to small N_Q). With few query rows the dQ kernel has one block per
+ * 256-row query block and slice, too few for the chip; here block (query block, slice, range)
+ * handles one contiguous range of 32-key tiles, writes its float32 partial dQ to the workspace,
+ * and a second kernel sums the ranges and rounds once to bfloat16. No atomics: the result is
+ * deterministic for a given n_splits and agrees with streamkl_bwd_dq to float32 summation
+ * order before the rounding.
+ *
+ * n_splits: requested ranges; <= 0 chooses streamkl_bwd_dq_splitk_default_splits(). The number
+ *   used is min(n_splits, visible key tiles, 1024), reduced so that no range is empty. With one
+ *   range this is streamkl_bwd_dq and the workspace is not touched.
+ * workspace: at least streamkl_bwd_dq_splitk_workspace_size(problem, n_splits) bytes of device
+ *   memory (0 for one range), 16-byte aligned, owned by the caller, overlapping no input or
+ *   output; contents on entry ignored, on return unspecified. It holds float32
+ *   [ranges used][batch * heads][n_q][head_dim].
+ * Other arguments and errors as streamkl_bwd_dq, plus STREAMKL_ERROR_INVALID_VALUE for a too
+ * small, misaligned or overlapping workspace.
+ */
+/* Ranges chosen for n_splits <= 0: about two blocks per CU with at least 16 key tiles per range;
+ * 1 when the dQ kernel already has 256 blocks or more. 0 for a NULL problem or sizes < 1. */
+int32_t streamkl_bwd_dq_splitk_default_splits(const streamkl_problem_t* problem);
+/* Workspace bytes streamkl_bwd_dq_splitk needs for this n_splits (0 with one range, and for a
+ * NULL problem or sizes < 1). */
+size_t streamkl_bwd_dq_splitk_workspace_size(const streamkl_problem_t* problem,
+                                             int32_t n_splits);
+streamkl_status_t streamkl_bwd_dq_splitk(const streamkl_problem_t* problem, int32_t setting,
+                                         const void* q1, const void* k1, const void* q2,
+                                         const void* k2, const float* lse1, const float* lse2,
+                                         const float* kl, const float* grad_kl, void* dq,
+                                         int32_t n_splits, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* streamkl_status_string(streamkl_status_t status);
 

@@ -13,6 +13,7 @@ Functions (names follow the C ABI):
   streamkl_bwd_fixP2(q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...)  -> (dq1, dk1)
   streamkl_bwd_dq(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...) -> dq (one kernel)
   streamkl_bwd_dk(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...) -> dk (one kernel)
+  streamkl_bwd_dq_splitk(setting, ..., n_splits=0)                 -> dq (key ranges + sum)
 Inputs are bfloat16 CUDA tensors [B, H, N, d] (the d axis contiguous, any other strides that
 are multiples of 8 elements); kl / lse / grad_kl are float32 [B, H, N_Q].
 """
@@ -29,8 +30,9 @@ STATUS = {0: "STREAMKL_SUCCESS", 1: "STREAMKL_ERROR_INVALID_VALUE",
 
 EXPORTS = ("streamkl_fwd", "streamkl_fwd_splitk", "streamkl_fwd_splitk_default_splits",
            "streamkl_fwd_splitk_workspace_size", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2",
-           "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_status_string",
-           "streamkl_last_error")
+           "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_bwd_dq_splitk",
+           "streamkl_bwd_dq_splitk_default_splits", "streamkl_bwd_dq_splitk_workspace_size",
+           "streamkl_status_string", "streamkl_last_error")
 
 
 class StreamKLError(RuntimeError):
@@ -73,8 +75,14 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.streamkl_bwd_fixP2.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, fp, vp, vp, vp]
     for name in ("streamkl_bwd_dq", "streamkl_bwd_dk"):
         getattr(L, name).argtypes = [pp, ctypes.c_int32, vp, vp, vp, vp, fp, fp, fp, fp, vp, vp]
+    L.streamkl_bwd_dq_splitk.argtypes = [pp, ctypes.c_int32, vp, vp, vp, vp, fp, fp, fp, fp, vp,
+                                         ctypes.c_int32, vp, ctypes.c_size_t, vp]
+    L.streamkl_bwd_dq_splitk_default_splits.argtypes = [pp]
+    L.streamkl_bwd_dq_splitk_default_splits.restype = ctypes.c_int32
+    L.streamkl_bwd_dq_splitk_workspace_size.argtypes = [pp, ctypes.c_int32]
+    L.streamkl_bwd_dq_splitk_workspace_size.restype = ctypes.c_size_t
     for name in ("streamkl_fwd", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2", "streamkl_bwd_dq",
-                 "streamkl_bwd_dk"):
+                 "streamkl_bwd_dk", "streamkl_bwd_dq_splitk"):
         getattr(L, name).restype = ctypes.c_int
     L.streamkl_status_string.argtypes = [ctypes.c_int]
     L.streamkl_status_string.restype = ctypes.c_char_p
@@ -259,3 +267,46 @@ def streamkl_bwd_dk(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=None
                     out=None):
     """dK of the free side only (one kernel): dk2 for setting 1, dk1 for setting 2."""
     return _bwd_one("dk", setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale, causal, out)
+
+
+def streamkl_bwd_dq_splitk_default_splits(q1, k1, scale=None, causal=False) -> int:
+    p = make_problem(q1, k1, scale, causal)
+    return int(lib().streamkl_bwd_dq_splitk_default_splits(ctypes.byref(p)))
+
+
+def streamkl_bwd_dq_splitk_workspace_size(q1, k1, n_splits=0, scale=None, causal=False) -> int:
+    p = make_problem(q1, k1, scale, causal)
+    return int(lib().streamkl_bwd_dq_splitk_workspace_size(ctypes.byref(p), int(n_splits)))
+
+
+def streamkl_bwd_dq_splitk(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=None,
+                           causal=False, n_splits=0, workspace=None, out=None):
+    """dQ of the free side with the keys split into ranges (few query rows); the workspace (a
+    uint8 CUDA tensor of at least streamkl_bwd_dq_splitk_workspace_size bytes) is allocated
+    here when not given."""
+    import torch
+    _check_inputs(q1, k1, q2, k2)
+    B, H, nq, _ = q1.shape
+    vecs = [("lse1", lse1), ("lse2", lse2), ("grad_kl", grad_kl)]
+    if setting == 2:
+        vecs.append(("kl", kl))
+    for n, t in vecs:
+        _rowvec(t, n, (B, H, nq))
+    ref = q2 if setting == 1 else q1
+    if out is None:
+        out = torch.empty(ref.shape, dtype=torch.bfloat16, device=ref.device)
+    if out.dtype != torch.bfloat16 or out.shape != ref.shape or not out.is_contiguous():
+        raise ValueError(f"dq must be a contiguous bfloat16 tensor of shape {tuple(ref.shape)}")
+    p = make_problem(q1, k1, scale, causal)
+    need = int(lib().streamkl_bwd_dq_splitk_workspace_size(ctypes.byref(p), int(n_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().streamkl_bwd_dq_splitk(ctypes.byref(p), setting, q1.data_ptr(), k1.data_ptr(),
+                                        q2.data_ptr(), k2.data_ptr(), lse1.data_ptr(),
+                                        lse2.data_ptr(), kl.data_ptr() if kl is not None else None,
+                                        grad_kl.data_ptr(), out.data_ptr(), int(n_splits),
+                                        workspace.data_ptr(), nbytes, _stream(q1)))
+    return out

@@ -143,9 +143,12 @@ __device__ __forceinline__ bf16x8 lds_a_frag(const uint16_t* lds, int row, int k
 // Block ids interleave slices: id = rank * n_slices + slice, so consecutive ids (which the
 // hardware deals round-robin to the 8 XCDs) are different slices and every block of one slice
 // shares the XCD (and L2) of that slice when n_slices is a multiple of 8.
+__device__ __forceinline__ void block_coords(int id, int n_slices, int& rank, int& slice) {
+  rank = id / n_slices;
+  slice = id - rank * n_slices;
+}
 __device__ __forceinline__ void block_coords(int n_slices, int& rank, int& slice) {
-  rank = blockIdx.x / n_slices;
-  slice = blockIdx.x - rank * n_slices;
+  block_coords(blockIdx.x, n_slices, rank, slice);
 }
 
 // ================================================================ forward
@@ -640,13 +643,19 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tr, int nb, int cc, in
 }
 
 // ---------------------------------------------------------------- dQ (query-major)
-template <int D, int SETTING, bool CAUSAL, bool SHARED_K>
+// With SPLIT, the key tiles are cut into nsplit ranges of split_tiles tiles and block
+// (query block, slice, range) writes its float32 partial dQ (already scaled by g * scale) to
+// part[range][slice][n_q][D]; dq_reduce_kernel sums the ranges. For few query rows this gives
+// the chip enough blocks; every partial is written (zeros for a range a block cannot see), so
+// the sum is deterministic and needs no atomics.
+template <int D, int SETTING, bool CAUSAL, bool SHARED_K, bool SPLIT = false>
 __global__ void __launch_bounds__(kBwdThreads, kBwdBlocksPerCU)
 dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
           const float* __restrict__ lse1, const float* __restrict__ lse2,
           const float* __restrict__ klv, const float* __restrict__ gv,
-          __bf16* __restrict__ dq_out, Shape s) {
+          __bf16* __restrict__ dq_out, Shape s, float* __restrict__ part = nullptr,
+          int nsplit = 1, int split_tiles = 0) {
   constexpr int BQ = 32 * kBwdWaves, KS = D / 16, NB = D / 32;
   constexpr int NTENS = SHARED_K ? 1 : 2;
   constexpr int FREE = SHARED_K ? 0 : 2 - SETTING;  // tensor index of K_free (side 2 for setting 1)
@@ -656,7 +665,8 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   __shared__ float gscale[kBwdWaves][32];
 
   int rank, slice;
-  block_coords(s.bh, rank, slice);
+  const int split = SPLIT ? (int)(blockIdx.x % nsplit) : 0;
+  block_coords(SPLIT ? (int)(blockIdx.x / nsplit) : (int)blockIdx.x, s.bh, rank, slice);
   const int nqb = (s.nq + BQ - 1) / BQ;
   const int qb = CAUSAL ? nqb - 1 - rank : rank;
   const int b = slice / s.heads, hd = slice - b * s.heads;
@@ -685,7 +695,9 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
 
   const int last_q = min(s.nq - 1, qb * BQ + BQ - 1);
   const int kend = CAUSAL ? min(s.nk, last_q + 1) : s.nk;
-  const int ntiles = (kend + kBT - 1) / kBT;
+  // key tiles [t0, t1) of this block
+  const int t0 = SPLIT ? split * split_tiles : 0;
+  const int t1 = SPLIT ? min((kend + kBT - 1) / kBT, t0 + split_tiles) : (kend + kBT - 1) / kBT;
   const bool wave_live = qw0 < s.nq;
 
   f32x16 dq[NB];
@@ -697,13 +709,15 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
     uint16_t* base = lds + buf * BUF;
     st.store(base, base + (NTENS - 1) * L::RM, base + NTENS * L::RM, FREE);
   };
-  st.load(K1, K2, s.k_sr, 0, s.nk);
-  stage_store(0);
-  if (ntiles > 1) st.load(K1, K2, s.k_sr, kBT, s.nk);
+  if (t0 < t1) {
+    st.load(K1, K2, s.k_sr, t0 * kBT, s.nk);
+    stage_store(0);
+    if (t0 + 1 < t1) st.load(K1, K2, s.k_sr, (t0 + 1) * kBT, s.nk);
+  }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const uint16_t* base = lds + (t & 1) * BUF;
+  for (int t = t0; t < t1; ++t) {
+    const uint16_t* base = lds + ((t - t0) & 1) * BUF;
     const uint16_t* kt1 = base;
     const uint16_t* kt2 = base + (NTENS - 1) * L::RM;
     const uint16_t* ktr = base + NTENS * L::RM;
@@ -770,9 +784,9 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           ds_block(std::true_type{}, rb);
       }
     }
-    if (t + 1 < ntiles) {
-      stage_store((t + 1) & 1);
-      if (t + 2 < ntiles) st.load(K1, K2, s.k_sr, (t + 2) * kBT, s.nk);
+    if (t + 1 < t1) {
+      stage_store((t + 1 - t0) & 1);
+      if (t + 2 < t1) st.load(K1, K2, s.k_sr, (t + 2) * kBT, s.nk);
     }
     __syncthreads();
   }
@@ -783,11 +797,38 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
     const int qr = qw0 + acc_row(r, h);
     if (qr < s.nq) {
       const float gsc = gscale[w][acc_row(r, h)];
-      __bf16* dst = dq_out + (obase + qr) * D + col;
+      if (SPLIT) {
+        float* dst = part + (((long long)split * s.bh) * s.nq + obase + qr) * D + col;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) dst[nb * 32] = static_cast<__bf16>(dq[nb][r] * gsc);
+        for (int nb = 0; nb < NB; ++nb) dst[nb * 32] = dq[nb][r] * gsc;
+      } else {
+        __bf16* dst = dq_out + (obase + qr) * D + col;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) dst[nb * 32] = static_cast<__bf16>(dq[nb][r] * gsc);
+      }
     }
   }
+}
+
+// Sum of the nsplit float32 partials of dQ (part[range][rows * D]), rounded once to bfloat16;
+// one thread per 4 consecutive elements.
+__global__ void __launch_bounds__(256)
+dq_reduce_kernel(const float* __restrict__ part, __bf16* __restrict__ dq, long long n4, int nsplit) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const float4* p = reinterpret_cast<const float4*>(part) + i;
+  float4 a = p[0];
+  for (int r = 1; r < nsplit; ++r) {
+    const float4 v = p[(long long)r * n4];
+    a.x += v.x;
+    a.y += v.y;
+    a.z += v.z;
+    a.w += v.w;
+  }
+  const bf16x2 lo = {static_cast<__bf16>(a.x), static_cast<__bf16>(a.y)};
+  const bf16x2 hi = {static_cast<__bf16>(a.z), static_cast<__bf16>(a.w)};
+  reinterpret_cast<uint2*>(dq)[i] =
+      make_uint2(__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi));
 }
 
 // ---------------------------------------------------------------- dK (key-major)
@@ -1134,6 +1175,69 @@ void launch_bwd(const Shape& s, const void* q1, const void* k1, const void* q2, 
                        (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dk, s);
 }
 
+// Key ranges of the split dQ kernel: ranges of whole 32-key tiles of the visible key span.
+struct DqSplitPlan {
+  int nsplit, split_tiles;
+};
+
+DqSplitPlan dq_split_plan(const streamkl_problem_t* p, int32_t n_splits) {
+  const int64_t nvis = p->causal && p->n_q < p->n_k ? p->n_q : p->n_k;
+  const int64_t ntiles = (nvis + kBT - 1) / kBT;
+  const int64_t blocks = p->batch * p->heads * ((p->n_q + 32 * kBwdWaves - 1) / (32 * kBwdWaves));
+  int64_t ns = n_splits;
+  if (ns <= 0) {
+    if (blocks >= 256) {
+      ns = 1;  // the dQ kernel already has a block for every CU
+    } else {
+      // about two blocks per CU, at least 16 key tiles per range
+      ns = (512 + blocks - 1) / blocks;
+      const int64_t cap = (ntiles + 15) / 16;
+      if (ns > cap) ns = cap;
+    }
+  }
+  if (ns > ntiles) ns = ntiles;
+  if (ns > 1024) ns = 1024;
+  if (ns < 1) ns = 1;
+  const int64_t per = (ntiles + ns - 1) / ns;
+  return {(int)((ntiles + per - 1) / per), (int)per};
+}
+
+size_t dq_split_workspace_bytes(const streamkl_problem_t* p, int nsplit) {
+  return nsplit > 1 ? (size_t)nsplit * p->batch * p->heads * p->n_q * p->head_dim * sizeof(float)
+                    : 0;
+}
+
+template <int D, int SET, bool CAUSAL, bool SK>
+void launch_dq_split(const Shape& s, const DqSplitPlan& plan, const void* q1, const void* k1,
+                     const void* q2, const void* k2, const float* l1, const float* l2,
+                     const float* kl, const float* g, void* dq, float* part, hipStream_t st) {
+  const int nqb = (s.nq + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
+  hipLaunchKernelGGL((dq_kernel<D, SET, CAUSAL, SK, true>), dim3(nqb * s.bh * plan.nsplit),
+                     dim3(kBwdThreads), 0, st, (const uint16_t*)q1, (const uint16_t*)k1,
+                     (const uint16_t*)q2, (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dq, s,
+                     part, plan.nsplit, plan.split_tiles);
+  const long long n4 = (long long)s.bh * s.nq * D / 4;
+  hipLaunchKernelGGL(dq_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                     (const float*)part, (__bf16*)dq, n4, plan.nsplit);
+}
+
+template <int SET>
+void dispatch_dq_split(int64_t d, bool causal, bool sk, const Shape& s, const DqSplitPlan& plan,
+                       const void* q1, const void* k1, const void* q2, const void* k2,
+                       const float* l1, const float* l2, const float* kl, const float* g,
+                       void* dq, float* part, hipStream_t st) {
+#define SKL_DQS(DD, C, S) \
+  launch_dq_split<DD, SET, C, S>(s, plan, q1, k1, q2, k2, l1, l2, kl, g, dq, part, st)
+  if (d == 64) {
+    if (causal) { if (sk) SKL_DQS(64, true, true); else SKL_DQS(64, true, false); }
+    else { if (sk) SKL_DQS(64, false, true); else SKL_DQS(64, false, false); }
+  } else {
+    if (causal) { if (sk) SKL_DQS(128, true, true); else SKL_DQS(128, true, false); }
+    else { if (sk) SKL_DQS(128, false, true); else SKL_DQS(128, false, false); }
+  }
+#undef SKL_DQS
+}
+
 template <int SET>
 void dispatch_bwd(int64_t d, bool causal, bool sk, const Shape& s, const void* q1,
                   const void* k1, const void* q2, const void* k2, const float* l1,
@@ -1154,7 +1258,8 @@ streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const voi
                              const void* k1, const void* q2, const void* k2, const float* lse1,
                              const float* lse2, const float* kl, const float* grad_kl, void* dq,
                              void* dk, bool want_dq, bool want_dk, hipStream_t stream,
-                             const char* what) {
+                             const char* what, const int32_t* dq_splits = nullptr,
+                             void* workspace = nullptr, size_t workspace_bytes = 0) {
   Shape s;
   streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
   if (st != STREAMKL_SUCCESS) return st;
@@ -1162,10 +1267,18 @@ streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const voi
   if (!lse1 || !lse2 || !grad_kl || (setting == 2 && !kl))
     return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": NULL lse / kl / grad pointer");
   const int64_t n = p->batch * p->heads * p->n_q;
-  Span outs[2];
+  DqSplitPlan plan = {1, 0};
+  if (dq_splits) plan = dq_split_plan(p, *dq_splits);
+  const size_t need = dq_split_workspace_bytes(p, plan.nsplit);
+  if (workspace_bytes < need)
+    return fail(STREAMKL_ERROR_INVALID_VALUE,
+                std::string(what) + ": workspace too small (" + std::to_string(workspace_bytes) +
+                    " < " + std::to_string(need) + " bytes)");
+  Span outs[3];
   int n_out = 0;
   if (want_dq) outs[n_out++] = flat_span(dq, n * p->head_dim, 2);
   if (want_dk) outs[n_out++] = flat_span(dk, p->batch * p->heads * p->n_k * p->head_dim, 2);
+  if (need > 0) outs[n_out++] = flat_span(workspace, (int64_t)need, 1);
   st = check_outputs(p, q1, k1, q2, k2, outs, n_out, what);
   if (st != STREAMKL_SUCCESS) return st;
   const Span vin[4] = {flat_span(lse1, n, 4), flat_span(lse2, n, 4), flat_span(grad_kl, n, 4),
@@ -1173,9 +1286,23 @@ streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const voi
   for (int i = 0; i < n_out; ++i)
     for (const Span& v : vin)
       if (overlaps(outs[i], v)) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": output overlaps an input");
+  if (plan.nsplit > 1 &&
+      (int64_t)plan.nsplit * p->batch * p->heads * ((p->n_q + 255) / 256) >= ((int64_t)1 << 31))
+    return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": grid too large");
   (void)hipGetLastError();
   void* dqp = want_dq ? dq : nullptr;
   void* dkp = want_dk ? dk : nullptr;
+  if (dqp && plan.nsplit > 1) {
+    float* part = static_cast<float*>(workspace);
+    if (setting == 1)
+      dispatch_dq_split<1>(p->head_dim, p->causal != 0, k1 == k2, s, plan, q1, k1, q2, k2, lse1,
+                           lse2, nullptr, grad_kl, dqp, part, stream);
+    else
+      dispatch_dq_split<2>(p->head_dim, p->causal != 0, k1 == k2, s, plan, q1, k1, q2, k2, lse1,
+                           lse2, kl, grad_kl, dqp, part, stream);
+    dqp = nullptr;
+  }
+  if (!dqp && !dkp) return check_launch(what);
   if (setting == 1)
     dispatch_bwd<1>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, lse1, lse2, nullptr,
                     grad_kl, dqp, dkp, stream);
@@ -1292,6 +1419,26 @@ streamkl_status_t streamkl_bwd_dk(const streamkl_problem_t* p, int32_t setting, 
                                   const float* grad_kl, void* dk, hipStream_t stream) {
   return bwd_common(p, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, nullptr, dk, false, true,
                     stream, "streamkl_bwd_dk");
+}
+
+int32_t streamkl_bwd_dq_splitk_default_splits(const streamkl_problem_t* p) {
+  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1) return 0;
+  return dq_split_plan(p, 0).nsplit;
+}
+
+size_t streamkl_bwd_dq_splitk_workspace_size(const streamkl_problem_t* p, int32_t n_splits) {
+  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1) return 0;
+  return dq_split_workspace_bytes(p, dq_split_plan(p, n_splits).nsplit);
+}
+
+streamkl_status_t streamkl_bwd_dq_splitk(const streamkl_problem_t* p, int32_t setting,
+                                         const void* q1, const void* k1, const void* q2,
+                                         const void* k2, const float* lse1, const float* lse2,
+                                         const float* kl, const float* grad_kl, void* dq,
+                                         int32_t n_splits, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common(p, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, dq, nullptr, true, false,
+                    stream, "streamkl_bwd_dq_splitk", &n_splits, workspace, workspace_bytes);
 }
 
 const char* streamkl_status_string(streamkl_status_t status) {

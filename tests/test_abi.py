@@ -147,3 +147,47 @@ def test_splitk_invalid_workspace():
     assert splitk(p, WS + 8, need, 1) == 1 and "aligned" in last_error()
     assert splitk(p, Q1 + 64, need, 1) == 1 and "overlap" in last_error()
     assert splitk(p, WS, need, 1, o=(O1, WS + 16, O3)) == 1
+
+
+def test_dq_splitk_plan_and_workspace():
+    L = skl.lib()
+    assert L.streamkl_bwd_dq_splitk_default_splits(None) == 0
+    assert L.streamkl_bwd_dq_splitk_workspace_size(None, 4) == 0
+    for nq, nk, causal in ((1, 65536, 0), (128, 65536, 0), (300, 5000, 1), (64, 80, 0),
+                           (40000, 40000, 0)):
+        p = good_problem()
+        p.n_q, p.n_k, p.causal = nq, nk, causal
+        nvis = min(nq, nk) if causal else nk
+        ntiles = (nvis + 31) // 32
+        per_range = 2 * nq * 128 * 4
+        d = L.streamkl_bwd_dq_splitk_default_splits(ctypes.byref(p))
+        assert 1 <= d <= ntiles
+        blocks = 2 * -(-nq // 256)
+        if blocks >= 256:
+            assert d == 1
+        ws0 = L.streamkl_bwd_dq_splitk_workspace_size(ctypes.byref(p), 0)
+        assert ws0 == (d * per_range if d > 1 else 0)
+        for req in (1, 2, 7, 10 ** 6):
+            ws = L.streamkl_bwd_dq_splitk_workspace_size(ctypes.byref(p), req)
+            used = ws // per_range if ws else 1
+            r = min(req, ntiles, 1024)
+            assert used == -(-ntiles // -(-ntiles // r))
+
+
+def test_dq_splitk_invalid_workspace():
+    p = good_problem()
+    p.n_k = 4096
+    L = skl.lib()
+    need = L.streamkl_bwd_dq_splitk_workspace_size(ctypes.byref(p), 4)
+    assert need > 0
+    WS = 0x7A000000
+
+    def call(ws, nbytes, n=4):
+        return L.streamkl_bwd_dq_splitk(ctypes.byref(p), 1, Q1, K1, Q2, K2, O1, O2, None, O3,
+                                        0x7C000000, n, ws, nbytes, None)
+    assert call(WS, need - 4) == 1 and "workspace too small" in last_error()
+    assert call(0, need) == 1
+    assert call(WS + 8, need) == 1 and "aligned" in last_error()
+    assert call(K1 + 64, need) == 1 and "overlap" in last_error()
+    # one range: no workspace needed, validation passes up to the launch (no GPU here)
+    assert L.streamkl_bwd_dq_splitk_workspace_size(ctypes.byref(p), 1) == 0

@@ -160,6 +160,83 @@ def cpu_baseline(w, x, target_s: float):
                       f"restricted to those rows, fp64 numpy, {pairs} visible pairs"}
 
 
+def small_nq(args):
+    """Few query rows (decode-like), 32 heads, 64K keys, d=128, non-causal, backward setting 1:
+    one JSON line per N_Q with the one-pass forward against the split-K forward and the
+    one-kernel dQ against the key-split dQ (dK alongside). The split-K forward reads every key
+    once, so its roofline is HBM bandwidth: algorithmic bytes = Q1, Q2, K1, K2 read once plus
+    KL, LSE1, LSE2 written, over the duration of the call (split kernel + merge kernel)."""
+    import numpy as np
+    import torch
+    import online_attention_kl_amd as skl
+    from workloads import Workload
+
+    dev = torch.device("cuda:0")
+    B, H, nk, d = 1, 32, 65536, 128
+    nqs = (1, 16, 128, 512)
+    w = Workload("small_nq", B, H, max(nqs), nk, d, False, (1,), 5, "perturb", sigma=0.5)
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = make_inputs(w)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k1, k2 = up(x["k1"]), up(x["k2"])
+    for nq in nqs:
+        q1 = up(x["q1"][:, :, :nq]).contiguous()
+        q2 = up(x["q2"][:, :, :nq]).contiguous()
+        g = torch.from_numpy(np.ascontiguousarray(x["g"][:, :, :nq])).to(dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = tuple(torch.empty((B, H, nq), **f32) for _ in range(3))
+        ns_f = skl.streamkl_fwd_splitk_default_splits(q1, k1)
+        wsf = torch.empty(skl.streamkl_fwd_splitk_workspace_size(q1, k1, 0), dtype=torch.uint8,
+                          device=dev)
+        skl.streamkl_fwd(q1, k1, q2, k2, out=out)
+        kl, l1, l2 = out
+        ns_q = skl.streamkl_bwd_dq_splitk_default_splits(q1, k1)
+        wsq = torch.empty(max(16, skl.streamkl_bwd_dq_splitk_workspace_size(q1, k1, 0)),
+                          dtype=torch.uint8, device=dev)
+        dq, dk = torch.empty_like(q2), torch.empty_like(k2)
+        fns = {
+            "fwd_one_pass": lambda: skl.streamkl_fwd(q1, k1, q2, k2, out=out),
+            "fwd_split_k": lambda: skl.streamkl_fwd_splitk(q1, k1, q2, k2, workspace=wsf, out=out),
+            "dq_one_kernel": lambda: skl.streamkl_bwd_dq(1, q1, k1, q2, k2, l1, l2, kl, g, out=dq),
+            "dq_split": lambda: skl.streamkl_bwd_dq_splitk(1, q1, k1, q2, k2, l1, l2, kl, g,
+                                                           workspace=wsq, out=dq),
+            "dk": lambda: skl.streamkl_bwd_dk(1, q1, k1, q2, k2, l1, l2, kl, g, out=dk),
+        }
+        ms = {}
+        for name, fn in fns.items():
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms[name] = e0.elapsed_time(e1) / args.steps
+        fbytes = B * H * (2 * nq * d * 2 + 2 * nk * d * 2 + 3 * nq * 4)
+        gbs = fbytes / (ms["fwd_split_k"] * 1e-3) / 1e9
+        line = {
+            "mode": "small_nq", "unit": "ms", "steps": args.steps, "warmup": args.warmup,
+            "data": "synthetic",
+            "config": {"workload": f"small_nq_{nq}", "batch": B, "heads": H, "n_q": nq,
+                       "n_k": nk, "head_dim": d, "causal": False, "backward_settings": [1],
+                       "fwd_ranges": ns_f, "dq_ranges": ns_q},
+            "ms": {k: round(v, 4) for k, v in ms.items()},
+            "speedup": {"fwd": round(ms["fwd_one_pass"] / ms["fwd_split_k"], 2),
+                        "dq": round(ms["dq_one_kernel"] / ms["dq_split"], 2),
+                        "backward": round((ms["dq_one_kernel"] + ms["dk"]) /
+                                          (ms["dq_split"] + ms["dk"]), 2)},
+            "roofline": {"kernel": "fwd_split_kernel + fwd_merge_kernel", "bound": "hbm",
+                         "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(gbs / 8000.0, 4), "traffic": None},
+        }
+        print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +247,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device copy of 1 GiB (reference for HBM byte counters)")
+    ap.add_argument("--small-nq", action="store_true",
+                    help="time the split-K forward and the key-split dQ against the one-pass "
+                         "paths on few-query-row shapes (one JSON line per shape)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter runs into profiles/hbm_traffic.json "
                          "(no GPU work)")
@@ -183,6 +263,9 @@ def main():
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.small_nq:
+        small_nq(args)
+        return
     w = WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     x = make_inputs(w)

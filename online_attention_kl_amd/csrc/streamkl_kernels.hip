@@ -18,22 +18,26 @@
 //    its own partial online state (m1, l1, m2, l2, acc) with no cross-lane traffic in the hot
 //    loop; the two lanes that share a query merge their states once at the end (the merge of
 //    two partial states is associative). The P1-weighted logit difference is accumulated from
-//    the unscaled dot products and scaled once at the end.
+//    the unscaled dot products and scaled once at the end. The running maxima are raised only on
+//    a lane's first tile and on masked tiles; an overflowed wave is recomputed exactly.
 //  * The dK kernel is key-major: a wave keeps its 32 key rows of K1 and K2 in registers and
 //    computes S = Q K^T, so dS^T comes out of the accumulator already in the A-operand layout
 //    of dK = dS^T Q. Symmetrically, the dQ kernel's dS is the A operand of dQ = dS K. The other
-//    operand of each gradient GEMM is read from the row-major LDS tile with
-//    ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit values across lanes, so no
-//    transposed copy is ever stored. The two backward kernels recompute S independently and
-//    never use atomics: results are deterministic.
-//  * Streamed tiles are staged in LDS with a 16-byte-chunk XOR swizzle (chunk ^ row) so that
-//    the 32 rows read by one MFMA operand load fall in distinct banks.
+//    operand of each gradient product is read from a transposed copy of the streamed tile that
+//    the block writes to LDS once per tile. The two backward kernels recompute S independently
+//    and never use atomics: results are deterministic.
+//  * Streamed tiles sit in double-buffered LDS with rows padded by 16 bytes, so the 16 rows read
+//    by one 16-byte operand load fall in distinct banks and every operand address is a base
+//    register plus an immediate.
 //  * exp and log use the hardware base-2 instructions; scale * log2(e) is folded into one FMA
 //    per element and the saved LSEs stay in natural-log units.
 //  * Causal (top-left) masking skips whole tiles past the frontier; only tiles that straddle
 //    the diagonal or the ragged end of a sequence take the masked path. Causal grids run the
 //    longest row blocks first, and block ids interleave the (batch, head) slices so that all
 //    blocks of one slice land on one XCD and share its L2.
+//  * Few query rows: a split-K forward (one wavefront per query block and key range, partial
+//    states merged by a second kernel) and a dQ kernel split over key ranges with a
+//    deterministic sum of the partials; both take a workspace from the caller.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

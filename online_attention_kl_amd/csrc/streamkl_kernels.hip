@@ -41,7 +41,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <cstdio>
 #include <string>
 #include <type_traits>
 
@@ -52,12 +51,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-constexpr int kThreads = 256;  // 4 waves of 64
-constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;  // finite stand-in for -inf in running maxima

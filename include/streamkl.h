@@ -81,6 +81,23 @@ streamkl_status_t streamkl_fwd(const streamkl_problem_t* problem,
                                float* kl, float* lse1, float* lse2, hipStream_t stream);
 
 /*
+ * Forward pass with OCP fp8 e4m3 inputs (mixed precision for the two Q K^T contractions,
+ * float32 state; the pages name lower-precision inputs as future work: gist.science/pt
+ * "Significancia" and agents-report, outlook). Same outputs and semantics as streamkl_fwd, with
+ * side t's logits S_t = scale * descale_t * Q_t K_t^T, where q_t, k_t hold e4m3 codes (1 byte,
+ * bias 7, no infinities) and descale_t is the product of the two tensors' dequantisation
+ * factors. Contractions run on v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) with float32
+ * accumulation; the online update is the bf16 forward's.
+ *
+ * Strides must be multiples of 16 elements (16 bytes); pointers 16-byte aligned.
+ * descale1, descale2: finite and > 0 (STREAMKL_ERROR_INVALID_VALUE otherwise).
+ */
+streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* problem, float descale1,
+                                   float descale2, const void* q1, const void* k1,
+                                   const void* q2, const void* k2, float* kl, float* lse1,
+                                   float* lse2, hipStream_t stream);
+
+/*
  * Split-K forward for few query rows (gist.science/pt "Resumo Tecnico", section "3. Otimizacoes
  * de Kernel de GPU", Split-K variant; its gain for small N_Q under "Resultados Experimentais",
  * ablation). Same outputs and semantics as streamkl_fwd, for any sizes.

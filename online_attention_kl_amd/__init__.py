@@ -7,6 +7,7 @@ HIP kernels; there is no fallback. If the library has not been built, `lib()` ra
 
 Functions (names follow the C ABI):
   streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False)           -> (kl, lse1, lse2)
+  streamkl_fwd_fp8(q1, k1, q2, k2, descale1=1, descale2=1, ...)   -> (kl, lse1, lse2), fp8 inputs
   streamkl_fwd_splitk(q1, k1, q2, k2, n_splits=0, ...)             -> (kl, lse1, lse2)
   streamkl_fwd_splitk_default_splits(q1, k1, ...), streamkl_fwd_splitk_workspace_size(...)
   streamkl_bwd_fixP1(q1, k1, q2, k2, lse1, lse2, grad_kl, ...)      -> (dq2, dk2)
@@ -28,7 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamkl
 STATUS = {0: "STREAMKL_SUCCESS", 1: "STREAMKL_ERROR_INVALID_VALUE",
           2: "STREAMKL_ERROR_NOT_SUPPORTED", 3: "STREAMKL_ERROR_HIP"}
 
-EXPORTS = ("streamkl_fwd", "streamkl_fwd_splitk", "streamkl_fwd_splitk_default_splits",
+EXPORTS = ("streamkl_fwd", "streamkl_fwd_fp8", "streamkl_fwd_splitk", "streamkl_fwd_splitk_default_splits",
            "streamkl_fwd_splitk_workspace_size", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2",
            "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_bwd_dq_splitk",
            "streamkl_bwd_dq_splitk_default_splits", "streamkl_bwd_dq_splitk_workspace_size",
@@ -64,6 +65,9 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     vp, fp = ctypes.c_void_p, ctypes.c_void_p
     pp = ctypes.POINTER(Problem)
     L.streamkl_fwd.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp]
+    L.streamkl_fwd_fp8.argtypes = [pp, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, fp, fp, fp,
+                                   vp]
+    L.streamkl_fwd_fp8.restype = ctypes.c_int
     L.streamkl_fwd_splitk.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, ctypes.c_int32, vp,
                                       ctypes.c_size_t, vp]
     L.streamkl_fwd_splitk.restype = ctypes.c_int
@@ -152,6 +156,33 @@ def streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False, out=None):
     _check(lib().streamkl_fwd(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
                               k2.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
                               out[2].data_ptr(), _stream(q1)))
+    return out
+
+
+def streamkl_fwd_fp8(q1, k1, q2, k2, descale1=1.0, descale2=1.0, scale=None, causal=False,
+                     out=None):
+    """Forward with float8_e4m3fn inputs: side t's logits are scale * descale_t * Q_t K_t^T."""
+    import torch
+    for name, t in (("q1", q1), ("k1", k1), ("q2", q2), ("k2", k2)):
+        if not t.is_cuda or t.dtype != torch.float8_e4m3fn or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be a float8_e4m3fn CUDA tensor [B, H, N, d] with a "
+                             "contiguous last dimension")
+    if q1.shape != q2.shape or q1.stride() != q2.stride() or k1.shape != k2.shape \
+            or k1.stride() != k2.stride() or k1.shape[:2] != q1.shape[:2] \
+            or k1.shape[3] != q1.shape[3]:
+        raise ValueError("q1/q2 and k1/k2 must match in shape and strides; q and k in batch, "
+                         "heads and head_dim")
+    B, H, nq, _ = q1.shape
+    if out is None:
+        out = tuple(torch.empty((B, H, nq), dtype=torch.float32, device=q1.device)
+                    for _ in range(3))
+    for n, t in zip(("kl", "lse1", "lse2"), out):
+        _rowvec(t, n, (B, H, nq))
+    p = make_problem(q1, k1, scale, causal)
+    _check(lib().streamkl_fwd_fp8(ctypes.byref(p), float(descale1), float(descale2),
+                                  q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(),
+                                  out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
+                                  _stream(q1)))
     return out
 
 

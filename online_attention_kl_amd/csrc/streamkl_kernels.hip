@@ -97,15 +97,18 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
 template <int D>
 constexpr int lds_pitch() { return D + 8; }
 
-template <int ROWS, int D, int NT>
+// Registers that stage ROWS rows of ROWB bytes from global memory into an LDS tile with a
+// pitch of ROWB + 16 bytes (the forward's key tiles, any element format).
+template <int ROWS, int ROWB, int NT>
 struct TileRegs {
-  static constexpr int CPR = D / 8;
-  static constexpr int N = ROWS * CPR / NT;
-  static_assert(N * NT == ROWS * CPR, "tile must split evenly over the block");
+  static constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
+  static constexpr int N = (ROWS * CPR + NT - 1) / NT;
+  static constexpr bool EVEN = N * NT == ROWS * CPR;  // else threads past the tile idle
   uint4 v[N];
 
-  // Rows row0.. of a [n_valid, D] matrix with row stride rstride; rows >= n_valid read as 0.
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, long long rstride,
+  // Rows row0.. of a [n_valid, ROWB bytes] matrix with a row stride of rstride bytes; rows
+  // >= n_valid read as 0.
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, long long rstride,
                                        int row0, int n_valid) {
     const bool full = row0 + ROWS <= n_valid;  // block-uniform: no per-row checks needed
 #pragma unroll
@@ -113,19 +116,19 @@ struct TileRegs {
       const int idx = threadIdx.x + i * NT;
       const int row = idx / CPR, c = idx % CPR;
       const int gr = row0 + row;
-      const uint16_t* src = base + (long long)gr * rstride + c * 8;
-      if (full || gr < n_valid)
+      const uint8_t* src = base + (long long)gr * rstride + c * 16;
+      if ((EVEN || idx < ROWS * CPR) && (full || gr < n_valid))
         v[i] = *reinterpret_cast<const uint4*>(src);
       else
         v[i] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  __device__ __forceinline__ void store(uint16_t* lds) const {
+  __device__ __forceinline__ void store(uint8_t* lds) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int idx = threadIdx.x + i * NT;
       const int row = idx / CPR, c = idx % CPR;
-      *reinterpret_cast<uint4*>(lds + row * lds_pitch<D>() + c * 8) = v[i];
+      if (EVEN || idx < ROWS * CPR) *reinterpret_cast<uint4*>(lds + row * (ROWB + 16) + c * 16) = v[i];
     }
   }
 };
@@ -150,9 +153,42 @@ __device__ __forceinline__ void block_coords(int n_slices, int& rank, int& slice
 }
 
 // ================================================================ forward
-// Each lane keeps its running state as a running maximum m_t (of the unscaled dot products) and
-// four interleaved partial sums of l1, l2 and acc, all relative to exp2(c * m_t) with
-// c = scale * log2(e): l_t = sum_j exp2(c (x_tj - m_t)), acc = sum_j exp2(c (x1j - m1)) (x1j - x2j).
+// Input formats of the forward's contractions. bf16: v_mfma_f32_32x32x16_bf16, 16 contraction
+// elements per instruction. fp8: OCP e4m3 through v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// (E8M0 = 127) block scales, 64 contraction elements per instruction. In both, a lane of the
+// A (B) operand holds row (column) lane % 32 and the contraction elements
+// (lane / 32) * KPER / 2 .. + KPER / 2 of the k-step in consecutive bytes, so one lane's operand
+// is a contiguous piece of one row of a row-major tile.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct Bf16In {
+  using Frag = bf16x8;
+  static constexpr int EB = 2, KPER = 16;
+  static __device__ __forceinline__ Frag load(const uint8_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+  }
+  static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) { return mfma(a, b, c); }
+};
+
+struct Fp8In {
+  using Frag = i32x8;
+  static constexpr int EB = 1, KPER = 64;
+  static __device__ __forceinline__ Frag load(const uint8_t* p) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint4 v = *reinterpret_cast<const uint4*>(p + 16);
+    return Frag{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  }
+  static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+// Each lane keeps its running state as a running maximum m_t (of the unscaled dot products x_t)
+// and NP interleaved partial sums of l1, l2 and acc, all relative to exp2(c_t m_t) with
+// c_t = scale * sigma_t * log2(e) (sigma_t = 1 for bf16 inputs, the dequantisation factor of
+// side t for fp8 inputs): l_t = sum_j exp2(c_t (x_tj - m_t)) and
+// acc = sum_j exp2(c_1 (x1j - m1)) (r12 x1j - x2j) with r12 = sigma_1 / sigma_2, so that the
+// logit difference S1 - S2 = scale * sigma_2 * (r12 x1 - x2) costs one FMA.
 //
 // The running maximum is raised only where it must be: on a lane's first tile, and on tiles that
 // take the masked path (the diagonal or the ragged end). Every other tile is accumulated against
@@ -165,20 +201,22 @@ __device__ __forceinline__ void block_coords(int n_slices, int& rank, int& slice
 // Adds one tile's exponentials to the partial sums against the current maxima (-c m_t = nb_t).
 // s1 / s2 hold the lane's unscaled dot products of the tile: RB blocks of 32 keys, 16 keys of
 // each block per lane. Masked entries are -inf and contribute 0.
-template <int RB, bool MASK>
+template <int RB, bool MASK, int NP>
 __device__ __forceinline__ void fwd_tile_accumulate(const f32x16 (&s1)[RB], const f32x16 (&s2)[RB],
-                                                    float c, float nb1, float nb2, float (&L1)[4],
-                                                    float (&L2)[4], float (&A)[4]) {
+                                                    float c1, float c2, float r12, float nb1,
+                                                    float nb2, float (&L1)[NP], float (&L2)[NP],
+                                                    float (&A)[NP]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float x1 = s1[rb][r], x2 = s2[rb][r];
-      const float p1 = exp2_hw(fmaf(x1, c, nb1));
-      const float p2 = exp2_hw(fmaf(x2, c, nb2));
+      const float p1 = exp2_hw(fmaf(x1, c1, nb1));
+      const float p2 = exp2_hw(fmaf(x2, c2, nb2));
       // masked entries have x1 = x2 = -inf and p1 = 0; their difference must not turn into NaN
-      const float dd = MASK ? (p1 > 0.f ? x1 - x2 : 0.f) : x1 - x2;
-      const int j = r & 3;
+      const float d12 = fmaf(x1, r12, -x2);
+      const float dd = MASK ? (p1 > 0.f ? d12 : 0.f) : d12;
+      const int j = r % NP;
       L1[j] += p1;
       L2[j] += p2;
       A[j] = fmaf(p1, dd, A[j]);
@@ -188,11 +226,11 @@ __device__ __forceinline__ void fwd_tile_accumulate(const f32x16 (&s1)[RB], cons
 
 // One tile with the running maxima raised to the tile's maxima first (the partial sums are
 // rescaled by exp2(c (m_old - m_new))). Applies the causal / ragged-end mask in place when MASK.
-template <int RB, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void fwd_tile_exact(f32x16 (&s1)[RB], f32x16 (&s2)[RB], float c,
-                                               int key0, int query, int nk, int h, float& m1,
-                                               float& m2, float& nb1, float& nb2, float (&L1)[4],
-                                               float (&L2)[4], float (&A)[4]) {
+template <int RB, bool CAUSAL, bool MASK, int NP>
+__device__ __forceinline__ void fwd_tile_exact(f32x16 (&s1)[RB], f32x16 (&s2)[RB], float c1,
+                                               float c2, float r12, int key0, int query, int nk,
+                                               int h, float& m1, float& m2, float& nb1, float& nb2,
+                                               float (&L1)[NP], float (&L2)[NP], float (&A)[NP]) {
   if (MASK) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -211,18 +249,18 @@ __device__ __forceinline__ void fwd_tile_exact(f32x16 (&s1)[RB], f32x16 (&s2)[RB
     mx1 = fmaxf(fmaxf(mx1, s1[rb][r]), s1[rb][r + 1]);
     mx2 = fmaxf(fmaxf(mx2, s2[rb][r]), s2[rb][r + 1]);
   }
-  const float a1 = exp2_hw((m1 - mx1) * c), a2 = exp2_hw((m2 - mx2) * c);
+  const float a1 = exp2_hw((m1 - mx1) * c1), a2 = exp2_hw((m2 - mx2) * c2);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NP; ++j) {
     L1[j] *= a1;
     L2[j] *= a2;
     A[j] *= a1;
   }
   m1 = mx1;
   m2 = mx2;
-  nb1 = -mx1 * c;
-  nb2 = -mx2 * c;
-  fwd_tile_accumulate<RB, MASK>(s1, s2, c, nb1, nb2, L1, L2, A);
+  nb1 = -mx1 * c1;
+  nb2 = -mx2 * c2;
+  fwd_tile_accumulate<RB, MASK, NP>(s1, s2, c1, c2, r12, nb1, nb2, L1, L2, A);
 }
 
 __device__ __forceinline__ bool non_finite(float x) {
@@ -240,63 +278,71 @@ constexpr int kFwdRB = 1;
 constexpr int kFwdSB = 64;
 constexpr int kFwdThreads = 64 * kFwdWaves;
 
-template <int D, bool CAUSAL, bool SHARED_K>
+// F: input format (Bf16In or Fp8In). q*/k* point at elements of that format; strides in the
+// Shape are in elements. Side t's logits are scale * sigma_t * Q_t K_t^T.
+template <class F, int D, bool CAUSAL, bool SHARED_K>
 __global__ void __launch_bounds__(kFwdThreads, kFwdBlocksPerCU)
-fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
-           const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
+fwd_kernel(const uint8_t* __restrict__ q1, const uint8_t* __restrict__ k1,
+           const uint8_t* __restrict__ q2, const uint8_t* __restrict__ k2,
            float* __restrict__ kl_out, float* __restrict__ lse1_out,
-           float* __restrict__ lse2_out, Shape s) {
-  constexpr int RB = kFwdRB, BK = 32 * RB, SB = kFwdSB, BQ = 32 * kFwdWaves, KS = D / 16;
+           float* __restrict__ lse2_out, Shape s, float sigma1, float sigma2) {
+  constexpr int EB = F::EB, KPER = F::KPER, KS = D / KPER;
+  constexpr int RB = kFwdRB, BK = 32 * RB, SB = kFwdSB, BQ = 32 * kFwdWaves;
   constexpr int NKT = SHARED_K ? 1 : 2;
   static_assert(SB % BK == 0, "a stage holds whole tiles");
-  constexpr int TILE = SB * lds_pitch<D>();
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * NKT * TILE];
+  constexpr int ROWB = D * EB, PB = ROWB + 16, TILE = SB * PB;  // bytes
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NKT * TILE];
 
   int rank, slice;
   block_coords(s.bh, rank, slice);
   const int nqb = (s.nq + BQ - 1) / BQ;
   const int qb = CAUSAL ? nqb - 1 - rank : rank;
   const int b = slice / s.heads, hd = slice - b * s.heads;
-  const uint16_t* Q1 = q1 + b * s.q_sb + hd * s.q_sh;
-  const uint16_t* Q2 = q2 + b * s.q_sb + hd * s.q_sh;
-  const uint16_t* K1 = k1 + b * s.k_sb + hd * s.k_sh;
-  const uint16_t* K2 = k2 + b * s.k_sb + hd * s.k_sh;
+  const uint8_t* Q1 = q1 + (b * s.q_sb + hd * s.q_sh) * EB;
+  const uint8_t* Q2 = q2 + (b * s.q_sb + hd * s.q_sh) * EB;
+  const uint8_t* K1 = k1 + (b * s.k_sb + hd * s.k_sh) * EB;
+  const uint8_t* K2 = k2 + (b * s.k_sb + hd * s.k_sh) * EB;
+  const long long qrs = s.q_sr * EB, krs = s.k_sr * EB;  // row strides in bytes
 
   const int l = lane_id(), w = wave_id(), h = l >> 5, col = l & 31;
   const int qw0 = qb * BQ + w * 32;
   const int query = qw0 + col;
   const int qrow = query < s.nq ? query : s.nq - 1;
+  // byte offset of this lane's operand within a k-step of a row
+  const int lane_off = h * (KPER / 2) * EB;
 
-  bf16x8 f1[KS], f2[KS];
+  typename F::Frag f1[KS], f2[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
-    f1[kk] = load_frag(Q1 + (long long)qrow * s.q_sr + kk * 16 + h * 8);
-    f2[kk] = load_frag(Q2 + (long long)qrow * s.q_sr + kk * 16 + h * 8);
+    f1[kk] = F::load(Q1 + qrow * qrs + kk * KPER * EB + lane_off);
+    f2[kk] = F::load(Q2 + qrow * qrs + kk * KPER * EB + lane_off);
   }
 
   const int last_q = min(s.nq - 1, qb * BQ + BQ - 1);
   const int kend = CAUSAL ? min(s.nk, last_q + 1) : s.nk;
   const int ntiles = (kend + BK - 1) / BK;
   const int nstages = (kend + SB - 1) / SB;
-  const float c = s.scale * kLog2e;
+  const float c1 = s.scale * sigma1 * kLog2e, c2 = s.scale * sigma2 * kLog2e;
+  const float r12 = sigma1 / sigma2;
   const bool wave_live = qw0 < s.nq;
 
+  constexpr int NP = 4;  // interleaved partial sums per quantity
   float m1 = kNegBig, m2 = kNegBig, nb1 = 0.f, nb2 = 0.f;
-  float L1[4] = {}, L2[4] = {}, A[4] = {};
-  TileRegs<SB, D, kFwdThreads> r1, r2;
-  r1.load(K1, s.k_sr, 0, s.nk);
-  if (!SHARED_K) r2.load(K2, s.k_sr, 0, s.nk);
+  float L1[NP] = {}, L2[NP] = {}, A[NP] = {};
+  TileRegs<SB, ROWB, kFwdThreads> r1, r2;
+  r1.load(K1, krs, 0, s.nk);
+  if (!SHARED_K) r2.load(K2, krs, 0, s.nk);
   r1.store(lds);
   if (!SHARED_K) r2.store(lds + TILE);
   if (nstages > 1) {
-    r1.load(K1, s.k_sr, SB, s.nk);
-    if (!SHARED_K) r2.load(K2, s.k_sr, SB, s.nk);
+    r1.load(K1, krs, SB, s.nk);
+    if (!SHARED_K) r2.load(K2, krs, SB, s.nk);
   }
   __syncthreads();
 
   f32x16 s1[RB], s2[RB];
   // S^T of the tile starting at row `row0` of the stage: 2 * RB independent accumulation chains
-  auto contract = [&](const uint16_t* kt1, const uint16_t* kt2, int row0) {
+  auto contract = [&](const uint8_t* kt1, const uint8_t* kt2, int row0) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       s1[rb] = f32x16{};
@@ -304,23 +350,24 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
     }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      bf16x8 a1[RB], a2[RB];
+      typename F::Frag a1[RB], a2[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        a1[rb] = lds_a_frag<D>(kt1, row0 + rb * 32 + col, kk, h);
-        if (!SHARED_K) a2[rb] = lds_a_frag<D>(kt2, row0 + rb * 32 + col, kk, h);
+        const int off = (row0 + rb * 32 + col) * PB + kk * KPER * EB + lane_off;
+        a1[rb] = F::load(kt1 + off);
+        if (!SHARED_K) a2[rb] = F::load(kt2 + off);
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        s1[rb] = mfma(a1[rb], f1[kk], s1[rb]);
-        s2[rb] = mfma(SHARED_K ? a1[rb] : a2[rb], f2[kk], s2[rb]);
+        s1[rb] = F::mma(a1[rb], f1[kk], s1[rb]);
+        s2[rb] = F::mma(SHARED_K ? a1[rb] : a2[rb], f2[kk], s2[rb]);
       }
     }
   };
 
   for (int st = 0; st < nstages; ++st) {
-    const uint16_t* kt1 = lds + (st & 1) * NKT * TILE;
-    const uint16_t* kt2 = kt1 + (NKT - 1) * TILE;
+    const uint8_t* kt1 = lds + (st & 1) * NKT * TILE;
+    const uint8_t* kt2 = kt1 + (NKT - 1) * TILE;
 #pragma unroll
     for (int sub = 0; sub < SB / BK; ++sub) {
       const int t = st * (SB / BK) + sub;
@@ -330,21 +377,23 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
         contract(kt1, kt2, sub * BK);
         const bool full = (key0 + BK <= s.nk) && (!CAUSAL || key0 + BK - 1 <= qw0);
         if (full && t > 0)
-          fwd_tile_accumulate<RB, false>(s1, s2, c, nb1, nb2, L1, L2, A);
+          fwd_tile_accumulate<RB, false, NP>(s1, s2, c1, c2, r12, nb1, nb2, L1, L2, A);
         else if (full)
-          fwd_tile_exact<RB, CAUSAL, false>(s1, s2, c, key0, query, s.nk, h, m1, m2, nb1, nb2, L1, L2, A);
+          fwd_tile_exact<RB, CAUSAL, false, NP>(s1, s2, c1, c2, r12, key0, query, s.nk, h, m1, m2,
+                                                nb1, nb2, L1, L2, A);
         else
-          fwd_tile_exact<RB, CAUSAL, true>(s1, s2, c, key0, query, s.nk, h, m1, m2, nb1, nb2, L1, L2, A);
+          fwd_tile_exact<RB, CAUSAL, true, NP>(s1, s2, c1, c2, r12, key0, query, s.nk, h, m1, m2,
+                                               nb1, nb2, L1, L2, A);
       }
     }
     if (st + 1 < nstages) {
       // the other buffer was last read in stage st - 1, before the previous barrier
-      uint16_t* nxt = lds + ((st + 1) & 1) * NKT * TILE;
+      uint8_t* nxt = lds + ((st + 1) & 1) * NKT * TILE;
       r1.store(nxt);
       if (!SHARED_K) r2.store(nxt + TILE);
       if (st + 2 < nstages) {
-        r1.load(K1, s.k_sr, (st + 2) * SB, s.nk);
-        if (!SHARED_K) r2.load(K2, s.k_sr, (st + 2) * SB, s.nk);
+        r1.load(K1, krs, (st + 2) * SB, s.nk);
+        if (!SHARED_K) r2.load(K2, krs, (st + 2) * SB, s.nk);
       }
     }
     __syncthreads();
@@ -360,23 +409,18 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   if (wave_live && __any(bad)) {
     m1 = m2 = kNegBig;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) L1[j] = L2[j] = A[j] = 0.f;
+    for (int j = 0; j < NP; ++j) L1[j] = L2[j] = A[j] = 0.f;
     const int wend = CAUSAL ? min(kend, qw0 + 32) : kend;
     for (int key0 = 0; key0 < wend; key0 += 32) {
       f32x16 x1[1] = {f32x16{}}, x2[1] = {f32x16{}};
-      const int key = key0 + col;
-      const bool kin = key < s.nk;
+      const long long ro = (long long)min(key0 + col, s.nk - 1) * krs + lane_off;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        bf16x8 a1 = {}, a2 = {};
-        if (kin) {
-          a1 = load_frag(K1 + (long long)key * s.k_sr + kk * 16 + h * 8);
-          a2 = load_frag(K2 + (long long)key * s.k_sr + kk * 16 + h * 8);
-        }
-        x1[0] = mfma(a1, f1[kk], x1[0]);
-        x2[0] = mfma(a2, f2[kk], x2[0]);
+        x1[0] = F::mma(F::load(K1 + ro + kk * KPER * EB), f1[kk], x1[0]);
+        x2[0] = F::mma(F::load(K2 + ro + kk * KPER * EB), f2[kk], x2[0]);
       }
-      fwd_tile_exact<1, CAUSAL, true>(x1, x2, c, key0, query, s.nk, h, m1, m2, nb1, nb2, L1, L2, A);
+      fwd_tile_exact<1, CAUSAL, true, NP>(x1, x2, c1, c2, r12, key0, query, s.nk, h, m1, m2, nb1,
+                                          nb2, L1, L2, A);
     }
     l1 = (L1[0] + L1[1]) + (L1[2] + L1[3]);
     l2 = (L2[0] + L2[1]) + (L2[2] + L2[3]);
@@ -389,15 +433,15 @@ fwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   const float oacc = __shfl_xor(acc, 32);
   if (h == 0 && query < s.nq) {
     const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
-    const float fa = exp2_hw((m1 - M1) * c), fb = exp2_hw((om1 - M1) * c);
-    const float ga = exp2_hw((m2 - M2) * c), gb = exp2_hw((om2 - M2) * c);
+    const float fa = exp2_hw((m1 - M1) * c1), fb = exp2_hw((om1 - M1) * c1);
+    const float ga = exp2_hw((m2 - M2) * c2), gb = exp2_hw((om2 - M2) * c2);
     const float L1s = l1 * fa + ol1 * fb;
     const float L2s = l2 * ga + ol2 * gb;
     const float As = acc * fa + oacc * fb;
-    const float lse1 = M1 * s.scale + log2_hw(L1s) * kLn2;
-    const float lse2 = M2 * s.scale + log2_hw(L2s) * kLn2;
+    const float lse1 = M1 * (s.scale * sigma1) + log2_hw(L1s) * kLn2;
+    const float lse2 = M2 * (s.scale * sigma2) + log2_hw(L2s) * kLn2;
     const long long o = (long long)slice * s.nq + query;
-    kl_out[o] = s.scale * As / L1s + (lse2 - lse1);
+    kl_out[o] = (s.scale * sigma2) * As / L1s + (lse2 - lse1);
     lse1_out[o] = lse1;
     lse2_out[o] = lse2;
   }
@@ -479,13 +523,13 @@ fwd_split_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
       if (key0 + 32 < kend) fetch(key0 + 32);
       const bool full = (key0 + 32 <= s.nk) && (!CAUSAL || key0 + 31 <= q0);
       if (pass == 0 && full && key0 > kbeg)
-        fwd_tile_accumulate<1, false>(x1, x2, c, nb1, nb2, L1, L2, A);
+        fwd_tile_accumulate<1, false, 4>(x1, x2, c, c, 1.f, nb1, nb2, L1, L2, A);
       else if (full)
-        fwd_tile_exact<1, CAUSAL, false>(x1, x2, c, key0, query, s.nk, h, m1, m2, nb1, nb2, L1,
-                                         L2, A);
+        fwd_tile_exact<1, CAUSAL, false, 4>(x1, x2, c, c, 1.f, key0, query, s.nk, h, m1, m2, nb1,
+                                            nb2, L1, L2, A);
       else
-        fwd_tile_exact<1, CAUSAL, true>(x1, x2, c, key0, query, s.nk, h, m1, m2, nb1, nb2, L1,
-                                        L2, A);
+        fwd_tile_exact<1, CAUSAL, true, 4>(x1, x2, c, c, 1.f, key0, query, s.nk, h, m1, m2, nb1,
+                                           nb2, L1, L2, A);
     }
     const bool bad = non_finite((L1[0] + L1[1]) + (L1[2] + L1[3])) ||
                      non_finite((L2[0] + L2[1]) + (L2[2] + L2[3])) ||
@@ -1033,7 +1077,7 @@ Span flat_span(const void* p, int64_t n, int64_t elem) {
 }
 
 streamkl_status_t validate(const streamkl_problem_t* p, const void* q1, const void* k1,
-                           const void* q2, const void* k2, Shape* s) {
+                           const void* q2, const void* k2, Shape* s, int elem_bytes = 2) {
   if (!p) return fail(STREAMKL_ERROR_INVALID_VALUE, "problem is NULL");
   if (p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1)
     return fail(STREAMKL_ERROR_INVALID_VALUE, "batch, heads, n_q and n_k must be >= 1");
@@ -1048,9 +1092,11 @@ streamkl_status_t validate(const streamkl_problem_t* p, const void* q1, const vo
   const int64_t nblk = (p->n_q > p->n_k ? p->n_q : p->n_k) / 128 + 1;
   if (nblk * p->batch * p->heads >= ((int64_t)1 << 31))
     return fail(STREAMKL_ERROR_INVALID_VALUE, "grid too large");
+  const int64_t sm = 16 / elem_bytes;  // strides keep every row 16-byte aligned
   for (int i = 0; i < 3; ++i) {
-    if (p->q_stride[i] < 0 || p->k_stride[i] < 0 || p->q_stride[i] % 8 || p->k_stride[i] % 8)
-      return fail(STREAMKL_ERROR_INVALID_VALUE, "strides must be non-negative multiples of 8");
+    if (p->q_stride[i] < 0 || p->k_stride[i] < 0 || p->q_stride[i] % sm || p->k_stride[i] % sm)
+      return fail(STREAMKL_ERROR_INVALID_VALUE, "strides must be non-negative multiples of " +
+                                                    std::to_string(sm) + " elements");
   }
   if (p->q_stride[2] < p->head_dim || p->k_stride[2] < p->head_dim)
     return fail(STREAMKL_ERROR_INVALID_VALUE, "row stride must be >= head_dim");
@@ -1075,12 +1121,12 @@ streamkl_status_t validate(const streamkl_problem_t* p, const void* q1, const vo
 
 streamkl_status_t check_outputs(const streamkl_problem_t* p, const void* q1, const void* k1,
                                 const void* q2, const void* k2, const Span* outs, int n_out,
-                                const char* what) {
+                                const char* what, int elem_bytes = 2) {
   const Span in[4] = {
-      tensor_span(q1, p->batch, p->heads, p->n_q, p->head_dim, p->q_stride, 2),
-      tensor_span(k1, p->batch, p->heads, p->n_k, p->head_dim, p->k_stride, 2),
-      tensor_span(q2, p->batch, p->heads, p->n_q, p->head_dim, p->q_stride, 2),
-      tensor_span(k2, p->batch, p->heads, p->n_k, p->head_dim, p->k_stride, 2)};
+      tensor_span(q1, p->batch, p->heads, p->n_q, p->head_dim, p->q_stride, elem_bytes),
+      tensor_span(k1, p->batch, p->heads, p->n_k, p->head_dim, p->k_stride, elem_bytes),
+      tensor_span(q2, p->batch, p->heads, p->n_q, p->head_dim, p->q_stride, elem_bytes),
+      tensor_span(k2, p->batch, p->heads, p->n_k, p->head_dim, p->k_stride, elem_bytes)};
   for (int i = 0; i < n_out; ++i) {
     if (outs[i].lo == 0) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": output pointer is NULL");
     if (outs[i].lo % 16) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": outputs must be 16-byte aligned");
@@ -1099,13 +1145,28 @@ streamkl_status_t check_launch(const char* what) {
   return STREAMKL_SUCCESS;
 }
 
-template <int D, bool CAUSAL, bool SK>
+template <class F, int D, bool CAUSAL, bool SK>
 void launch_fwd(const Shape& s, const void* q1, const void* k1, const void* q2, const void* k2,
-                float* kl, float* l1, float* l2, hipStream_t st) {
+                float* kl, float* l1, float* l2, float sigma1, float sigma2, hipStream_t st) {
   const int nqb = (s.nq + 32 * kFwdWaves - 1) / (32 * kFwdWaves);
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SK>), dim3(nqb * s.bh), dim3(kFwdThreads), 0, st,
-                     (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
-                     (const uint16_t*)k2, kl, l1, l2, s);
+  hipLaunchKernelGGL((fwd_kernel<F, D, CAUSAL, SK>), dim3(nqb * s.bh), dim3(kFwdThreads), 0, st,
+                     (const uint8_t*)q1, (const uint8_t*)k1, (const uint8_t*)q2,
+                     (const uint8_t*)k2, kl, l1, l2, s, sigma1, sigma2);
+}
+
+template <class F>
+void dispatch_fwd(int64_t d, bool causal, bool sk, const Shape& s, const void* q1, const void* k1,
+                  const void* q2, const void* k2, float* kl, float* l1, float* l2, float sigma1,
+                  float sigma2, hipStream_t st) {
+#define SKL_FWD(DD, C, S) launch_fwd<F, DD, C, S>(s, q1, k1, q2, k2, kl, l1, l2, sigma1, sigma2, st)
+  if (d == 64) {
+    if (causal) { if (sk) SKL_FWD(64, true, true); else SKL_FWD(64, true, false); }
+    else { if (sk) SKL_FWD(64, false, true); else SKL_FWD(64, false, false); }
+  } else {
+    if (causal) { if (sk) SKL_FWD(128, true, true); else SKL_FWD(128, true, false); }
+    else { if (sk) SKL_FWD(128, false, true); else SKL_FWD(128, false, false); }
+  }
+#undef SKL_FWD
 }
 
 // Key ranges of the split-K forward: n_splits requested (<= 0: chosen here) -> tiles per range
@@ -1325,17 +1386,28 @@ streamkl_status_t streamkl_fwd(const streamkl_problem_t* p, const void* q1, cons
   st = check_outputs(p, q1, k1, q2, k2, outs, 3, "streamkl_fwd");
   if (st != STREAMKL_SUCCESS) return st;
   (void)hipGetLastError();
-  const bool sk = k1 == k2, causal = p->causal != 0;
-#define SKL_FWD(DD, C, S) launch_fwd<DD, C, S>(s, q1, k1, q2, k2, kl, lse1, lse2, stream)
-  if (p->head_dim == 64) {
-    if (causal) { if (sk) SKL_FWD(64, true, true); else SKL_FWD(64, true, false); }
-    else { if (sk) SKL_FWD(64, false, true); else SKL_FWD(64, false, false); }
-  } else {
-    if (causal) { if (sk) SKL_FWD(128, true, true); else SKL_FWD(128, true, false); }
-    else { if (sk) SKL_FWD(128, false, true); else SKL_FWD(128, false, false); }
-  }
-#undef SKL_FWD
+  dispatch_fwd<Bf16In>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, kl, lse1, lse2,
+                       1.f, 1.f, stream);
   return check_launch("streamkl_fwd");
+}
+
+streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* p, float descale1, float descale2,
+                                   const void* q1, const void* k1, const void* q2, const void* k2,
+                                   float* kl, float* lse1, float* lse2, hipStream_t stream) {
+  Shape s;
+  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s, 1);
+  if (st != STREAMKL_SUCCESS) return st;
+  if (!(descale1 > 0.f) || !(descale1 < __builtin_huge_valf()) || !(descale2 > 0.f) ||
+      !(descale2 < __builtin_huge_valf()))
+    return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_fwd_fp8: descales must be finite and > 0");
+  const int64_t n = p->batch * p->heads * p->n_q;
+  const Span outs[3] = {flat_span(kl, n, 4), flat_span(lse1, n, 4), flat_span(lse2, n, 4)};
+  st = check_outputs(p, q1, k1, q2, k2, outs, 3, "streamkl_fwd_fp8", 1);
+  if (st != STREAMKL_SUCCESS) return st;
+  (void)hipGetLastError();
+  dispatch_fwd<Fp8In>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1,
+                      q2, k2, kl, lse1, lse2, descale1, descale2, stream);
+  return check_launch("streamkl_fwd_fp8");
 }
 
 int32_t streamkl_fwd_splitk_default_splits(const streamkl_problem_t* p) {

@@ -1,5 +1,6 @@
 """The seeded input generator: bf16 rounding, determinism, slice independence, shapes."""
 import numpy as np
+import pytest
 import torch
 
 from workloads import (WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs, slice_inputs,
@@ -46,3 +47,25 @@ def test_visible_pairs():
     assert visible_pairs(WORKLOADS["asym_2k_32k_d64"]) == 4 * 32 * 2048 * 32768
     w = WORKLOADS["tiny_256_d64"].with_(n_q=5, n_k=3, causal=True)
     assert visible_pairs(w) == 1 + 2 + 3 + 3 + 3
+
+
+def test_fp8_e4m3_codes_match_torch():
+    """The generator's e4m3 rounding (ties to even) and decoding agree with PyTorch's own
+    float8_e4m3fn conversion on random values, every representable value and every midpoint."""
+    import torch
+    from workloads import f32_to_fp8_e4m3_bits, fp8_e4m3_bits_to_f32
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * s
+                        for s in (1e-3, 0.1, 1.0, 10.0, 100.0)])
+    x = x[np.abs(x) < 448]
+    codes = np.arange(256, dtype=np.uint8)
+    vals = fp8_e4m3_bits_to_f32(codes)
+    pos = np.unique(vals[np.isfinite(vals) & (vals >= 0)])
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([x, pos, -pos, mids, -mids])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(f32_to_fp8_e4m3_bits(x), ref)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert np.all((vals == dec) | (np.isnan(vals) & np.isnan(dec)))
+    with pytest.raises(ValueError):
+        f32_to_fp8_e4m3_bits(np.array([470.0], np.float32))

@@ -1,8 +1,8 @@
 """Seeded synthetic inputs for StreamKL, shared by the HIP path's tests/bench and the oracle.
 
 This module holds no part of the method's arithmetic: it only draws random numbers, rounds
-them to bfloat16 bit patterns (round-to-nearest-even) and decodes those bit patterns back to
-float32. Both sides (oracle and GPU) read the same bytes produced here.
+them to bfloat16 or fp8 e4m3 bit patterns (round-to-nearest-even) and decodes those bit patterns
+back to float32. Both sides (oracle and GPU) read the same bytes produced here.
 
 Workload shapes follow the pages' setting: attention distillation over contexts of 4K-512K
 tokens with 32 heads (gist.science/pt "Resultados Experimentais"; 64K x 32 heads in BF16 in
@@ -24,7 +24,8 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "f32_to_bf16_bits", "bf16_bits_to_f32",
-    "slice_inputs", "make_inputs", "visible_pairs",
+    "slice_inputs", "make_inputs", "visible_pairs", "f32_to_fp8_e4m3_bits",
+    "fp8_e4m3_bits_to_f32", "fp8_inputs",
 ]
 
 
@@ -183,3 +184,59 @@ def make_inputs(w: Workload, g_mode: str | None = None, threads: int | None = No
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(fill, range(B * H)))
     return {"q1": q1, "k1": k1, "q2": q2, "k2": k2, "g": g}
+
+
+# ---------------------------------------------------------------- fp8 e4m3 (OCP, "fn" variant)
+# 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; subnormals below 2^-6 in steps of 2^-9;
+# no infinities; the largest finite value is 448 = 1.75 * 2^8.
+FP8_E4M3_MAX = 448.0
+
+
+def f32_to_fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest e4m3 code (ties to even). Values that would round
+    past 448 are rejected (no saturation, no NaN codes are produced)."""
+    x = np.asarray(x, np.float32)
+    a = np.abs(x).astype(np.float64)
+    if np.any(~np.isfinite(a)) or np.any(a >= 464.0):  # 464 = halfway from 448 to 512
+        raise ValueError("value outside the e4m3 range")
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -9)))
+    e = np.clip(e, -6, 8)                   # binade; -6 also covers the subnormals
+    quantum = np.exp2(e - 3)                # spacing of the 8 mantissa steps in that binade
+    m = np.rint(a / quantum) * quantum      # round half to even
+    # re-encode (a carry into the next binade stays exact)
+    e2 = np.floor(np.log2(np.maximum(m, 2.0 ** -9)))
+    normal = m >= 2.0 ** -6
+    exp_field = np.where(normal, e2 + 7, 0)
+    mant = np.where(normal, m / np.exp2(e2) - 1.0, m / 2.0 ** -9) * np.where(normal, 8.0, 1.0)
+    mant = np.where(m == 0, 0, mant)
+    code = (exp_field.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def fp8_e4m3_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Decode e4m3 codes to float32 (exact); NaN codes (0x7f, 0xff) decode to NaN."""
+    b = np.asarray(b, np.uint8).astype(np.int64)
+    e = (b >> 3) & 15
+    m = b & 7
+    v = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    v = np.where((b & 0x7F) == 0x7F, np.nan, v)
+    return np.where(b & 0x80, -v, v).astype(np.float32)
+
+
+def fp8_inputs(w: Workload, gain: tuple = (4.0, 4.0, 2.0, 2.0), threads: int | None = None) -> dict:
+    """The workload's bf16 inputs (same seed and draws) multiplied by per-tensor power-of-two
+    gains and rounded to e4m3 codes: q1, k1, q2, k2 as uint8 arrays plus g. Side t's
+    dequantisation factor is 1 / (gain_q gain_k), returned as "descale1", "descale2"."""
+    x = make_inputs(w, threads=threads)
+    out = {"g": x["g"]}
+    names = ("q1", "k1", "q2", "k2")
+    for n, gn in zip(names, gain):
+        if n == "k2" and x["k2"] is x["k1"] and gain[3] == gain[1]:
+            out["k2"] = out["k1"]
+            continue
+        f = bf16_bits_to_f32(x[n]).reshape(x[n].shape)
+        out[n] = f32_to_fp8_e4m3_bits(f * np.float32(gn))
+    out["descale1"] = 1.0 / (gain[0] * gain[1])
+    out["descale2"] = 1.0 / (gain[2] * gain[3])
+    return out

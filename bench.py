@@ -237,6 +237,73 @@ def small_nq(args):
         print(json.dumps(line), flush=True)
 
 
+def fp8_mode(args):
+    """The fp8 e4m3 forward against the bf16 forward on the workload's inputs (bf16 values
+    times a gain of 4, rounded to e4m3 on the device; descale 1/16 per side): per-launch time
+    from HIP events, the fp8 forward against the fp8 MFMA roofline (same algorithmic 4 d flop
+    per visible pair), and the effect of the fp8 rounding of the inputs on KL and LSE over every
+    row (fp8 result minus bf16 result)."""
+    import numpy as np
+    import torch
+    import online_attention_kl_amd as skl
+
+    w = WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    b = [up(x["q1"]), up(x["k1"]), up(x["q2"])]
+    b.append(b[1] if x["k2"] is x["k1"] else up(x["k2"]))
+    gain = 4.0
+    f8 = [(t.float() * gain).to(torch.float8_e4m3fn) for t in b[:3]]
+    f8.append(f8[1] if b[3] is b[1] else (b[3].float() * gain).to(torch.float8_e4m3fn))
+    ds = 1.0 / (gain * gain)
+    B, H, nq = w.batch, w.heads, w.n_q
+    ob = tuple(torch.empty((B, H, nq), dtype=torch.float32, device=dev) for _ in range(3))
+    of = tuple(torch.empty((B, H, nq), dtype=torch.float32, device=dev) for _ in range(3))
+    fns = {"fwd_bf16": lambda: skl.streamkl_fwd(*b, causal=w.causal, out=ob),
+           "fwd_fp8": lambda: skl.streamkl_fwd_fp8(*f8, ds, ds, causal=w.causal, out=of)}
+    ms = {}
+    for name, fn in fns.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / args.steps
+    pairs = visible_pairs(w)
+    flop = 4 * w.head_dim * pairs
+    tf = flop / (ms["fwd_fp8"] * 1e-3) / 1e12
+    dkl = (of[0] - ob[0]).abs()
+    dl1 = (of[1] - ob[1]).abs()
+    kl_mag = ob[0].abs()
+    line = {
+        "mode": "fp8", "unit": "ms", "steps": args.steps, "warmup": args.warmup,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "n_q": nq, "n_k": w.n_k,
+                   "head_dim": w.head_dim, "causal": w.causal, "input_gain": gain,
+                   "descale": ds},
+        "ms": {k: round(v, 3) for k, v in ms.items()},
+        "speedup_vs_bf16": round(ms["fwd_bf16"] / ms["fwd_fp8"], 3),
+        "roofline": {"kernel": "fwd_kernel<fp8>", "bound": "mfma", "achieved": round(tf, 1),
+                     "peak": 5000.0, "unit": "TFLOP/s", "frac": round(tf / 5000.0, 4),
+                     "traffic": None},
+        "fp8_minus_bf16": {
+            "kl_abs_max": float(dkl.max()), "kl_abs_mean": float(dkl.mean()),
+            "kl_rel_median": float((dkl / kl_mag.clamp_min(1e-6)).median()),
+            "kl_mean_bf16": float(ob[0].mean()),
+            "lse1_abs_max": float(dl1.max()), "lse1_abs_mean": float(dl1.mean())},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +317,9 @@ def main():
     ap.add_argument("--small-nq", action="store_true",
                     help="time the split-K forward and the key-split dQ against the one-pass "
                          "paths on few-query-row shapes (one JSON line per shape)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the fp8 e4m3 forward against the bf16 forward on --workload and "
+                         "report the effect of the fp8 input rounding on KL and LSE")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter runs into profiles/hbm_traffic.json "
                          "(no GPU work)")
@@ -265,6 +335,9 @@ def main():
 
     if args.small_nq:
         small_nq(args)
+        return
+    if args.fp8:
+        fp8_mode(args)
         return
     w = WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)

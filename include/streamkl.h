@@ -82,8 +82,8 @@ streamkl_status_t streamkl_fwd(const streamkl_problem_t* problem,
 
 /*
  * Forward pass with OCP fp8 e4m3 inputs (mixed precision for the two Q K^T contractions,
- * float32 state; the pages name lower-precision inputs as future work: gist.science/pt
- * "Significancia" and agents-report, outlook). Same outputs and semantics as streamkl_fwd, with
+ * float32 state; mixed precision is named as future work in the agents-report article's
+ * conclusion). Same outputs and semantics as streamkl_fwd, with
  * side t's logits S_t = scale * descale_t * Q_t K_t^T, where q_t, k_t hold e4m3 codes (1 byte,
  * bias 7, no infinities) and descale_t is the product of the two tensors' dequantisation
  * factors. Contractions run on v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) with float32

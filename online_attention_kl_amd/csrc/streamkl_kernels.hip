@@ -886,8 +886,11 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   using L = BwdLayout<D>;
   constexpr int BUF = 2 * L::RM + L::TR;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
-  // per query of a tile: bias of P1, bias of P2 (setting 1) or LSE2 - LSE1 - KL (setting 2), g
+  // Per query of a tile: the exponent bias of P1 and of P2 (setting 1) or LSE2 - LSE1 - KL
+  // (setting 2), with log2 |g| folded into the exponent biases (g P = sign(g) 2^(y + log2 |g|)),
+  // and sign(g). Tiles whose g are all >= 0 (flag qneg = 0) never read the sign.
   __shared__ __attribute__((aligned(16))) float qa[2][3][kBT];
+  __shared__ int qneg[2];
 
   int rank, slice;
   block_coords(s.bh, rank, slice);
@@ -922,18 +925,27 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   for (int nb = 0; nb < NB; ++nb) dk[nb] = f32x16{};
 
   BwdStage<D, 2> st;
-  float cq0 = 0.f, cq1 = 0.f, cq2 = 0.f;  // constants of query tile row threadIdx.x (< kBT)
+  // constants of query tile row threadIdx.x (< kBT, lanes of wave 0) and the tile's sign flag
+  float cq0 = 0.f, cq1 = 0.f, cq2 = 0.f;
+  int cneg = 0;
   auto load_tile = [&](int t) {
     st.load(Q1, Q2, s.q_sr, t * kBT, s.nq);
     if (threadIdx.x < kBT) {
       const int q = t * kBT + threadIdx.x;
-      cq0 = cq1 = cq2 = 0.f;  // rows past n_q: g = 0, so they contribute nothing
+      // rows past n_q (and rows with g = 0) get P = 0: bias -inf
+      cq0 = -kInf;
+      cq1 = SETTING == 1 ? -kInf : 0.f;
+      cq2 = 1.f;
+      bool neg = false;
       if (q < s.nq) {
-        const float x1 = lse1[rbase + q], x2 = lse2[rbase + q];
-        cq0 = -x1 * kLog2e;
-        cq1 = SETTING == 1 ? -x2 * kLog2e : (x2 - x1) - klv[rbase + q];
-        cq2 = gv[rbase + q];
+        const float x1 = lse1[rbase + q], x2 = lse2[rbase + q], g = gv[rbase + q];
+        const float lg = g != 0.f ? log2_hw(fabsf(g)) : -kInf;
+        cq0 = fmaf(-x1, kLog2e, lg);
+        cq1 = SETTING == 1 ? fmaf(-x2, kLog2e, lg) : (x2 - x1) - klv[rbase + q];
+        cq2 = g < 0.f ? -1.f : 1.f;
+        neg = g < 0.f;
       }
+      cneg = __any(neg) ? 1 : 0;
     }
   };
   auto stage_store = [&](int buf) {
@@ -943,6 +955,7 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
       qa[buf][0][threadIdx.x] = cq0;
       qa[buf][1][threadIdx.x] = cq1;
       qa[buf][2][threadIdx.x] = cq2;
+      if (threadIdx.x == 0) qneg[buf] = cneg;
     }
   };
   const int ntiles = t_hi >= t_lo ? t_hi - t_lo + 1 : 0;
@@ -985,8 +998,9 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
       }
       // dS^T of one 32-query block and its dK product; the element mask is compiled only into
       // the variant used on tiles that straddle the diagonal or the ragged end
-      auto ds_block = [&](auto maskc, int rb) {
+      auto ds_block = [&](auto maskc, auto signc, int rb) {
         constexpr bool MASK = decltype(maskc)::value;
+        constexpr bool SIGNED = decltype(signc)::value;  // some g < 0 in this tile
         float ds[16];
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
@@ -994,7 +1008,8 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           const int qi = rb * 32 + rq * 8 + h * 4;
           const float4 va0 = *reinterpret_cast<const float4*>(&qa[buf][0][qi]);
           const float4 va1 = *reinterpret_cast<const float4*>(&qa[buf][1][qi]);
-          const float4 va2 = *reinterpret_cast<const float4*>(&qa[buf][2][qi]);
+          const float4 va2 = SIGNED ? *reinterpret_cast<const float4*>(&qa[buf][2][qi])
+                                    : make_float4(1.f, 1.f, 1.f, 1.f);
           const float c0[4] = {va0.x, va0.y, va0.z, va0.w};
           const float c1[4] = {va1.x, va1.y, va1.z, va1.w};
           const float c2[4] = {va2.x, va2.y, va2.z, va2.w};
@@ -1009,11 +1024,14 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
               e1 = ok ? e1 : -kInf;
               e2 = ok ? e2 : -kInf;
             }
+            // g P1 and g P2 with |g| inside the exponent
             const float p1 = exp2_hw(fmaf(e1, c, c0[j]));
+            float v;
             if (SETTING == 1)
-              ds[r] = c2[j] * (exp2_hw(fmaf(e2, c, c1[j])) - p1);
+              v = exp2_hw(fmaf(e2, c, c1[j])) - p1;
             else
-              ds[r] = c2[j] * (p1 * fmaf(d12, s.scale, c1[j]));
+              v = p1 * fmaf(d12, s.scale, c1[j]);
+            ds[r] = SIGNED ? c2[j] * v : v;
           }
         }
 #pragma unroll
@@ -1024,13 +1042,17 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
             dk[nb] = mfma(a, tr_frag(qtr, nb, rb * 2 + cc, col, h), dk[nb]);
         }
       };
+      const bool signed_tile = qneg[buf] != 0;
 #pragma unroll
       for (int rb = 0; rb < kBwdRB; ++rb) {
         const int qb0 = qt0 + rb * 32;
-        if ((qb0 + 32 <= s.nq) && (!CAUSAL || qb0 >= kw0 + 31))
-          ds_block(std::false_type{}, rb);
+        const bool full = (qb0 + 32 <= s.nq) && (!CAUSAL || qb0 >= kw0 + 31);
+        // two variants only (a third costs registers): tiles that straddle the diagonal or
+        // the ragged end, or hold a negative g, take the masked variant that applies the sign
+        if (full && !signed_tile)
+          ds_block(std::false_type{}, std::false_type{}, rb);
         else
-          ds_block(std::true_type{}, rb);
+          ds_block(std::true_type{}, std::true_type{}, rb);
       }
     }
     if (i + 1 < ntiles) {

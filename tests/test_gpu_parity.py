@@ -231,3 +231,55 @@ def test_large_logit_range(boost, causal):
         # along v): there the rounding of dS to bf16, not the kernel, sets the error
         check_grads(w, r, setting, dq, dk, rdq, rdk, lmax,
                     extra=bf16_ds_bound(setting, r, scale, causal))
+
+
+def signed_g(B, H, nq, seed):
+    """Upstream gradients of both signs and of very different sizes, laid out so that query tiles
+    of 32 rows come in every kind: all positive, one negative row, all zero, all negative, mixed
+    with zeros. Magnitudes are log-uniform over [1e-3, 1e3]."""
+    rng = np.random.default_rng(seed)
+    mag = 10.0 ** rng.uniform(-3, 3, (B, H, nq))
+    sign = np.where(rng.random((B, H, nq)) < 0.5, -1.0, 1.0)
+    g = mag * sign
+    kinds = ["pos", "one_neg", "zero", "neg", "mixed"] * (nq // 160 + 1)
+    for t0, kind in zip(range(0, nq, 32), kinds):
+        blk = slice(t0, min(nq, t0 + 32))
+        if kind == "pos":
+            g[..., blk] = np.abs(g[..., blk])
+        elif kind == "one_neg":
+            g[..., blk] = np.abs(g[..., blk])
+            g[..., t0 + min(5, nq - 1 - t0)] *= -1
+        elif kind == "zero":
+            g[..., blk] = 0.0
+        elif kind == "neg":
+            g[..., blk] = -np.abs(g[..., blk])
+        else:
+            g[..., t0:min(nq, t0 + 32):7] = 0.0
+    g[..., nq - 3:] = 0.0
+    return g.astype(np.float32)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 300, 257, 128, True), (1, 1, 257, 400, 64, False),
+                                   (2, 1, 640, 640, 128, True)], ids=shape_id)
+def test_signed_upstream_gradient(shape):
+    """Both backward settings with g of both signs, zeros and six decades of magnitude (the dK
+    kernel folds log2 |g| into its exponents and applies the sign only on tiles that need it)."""
+    announce(f"signed g {shape_id(shape)}")
+    w, d, r = make(shape, "perturb")
+    g = signed_g(*shape[:3], seed=5)
+    d["g"], r["g"] = torch.from_numpy(g).cuda(), g.astype(np.float64)
+    kl, l1, l2 = skl.streamkl_fwd(d["q1"], d["k1"], d["q2"], d["k2"], causal=w.causal)
+    rk, r1, r2 = oracle.forward(r["q1"], r["k1"], r["q2"], r["k2"], w.scale, w.causal)
+    lmax = max(np.abs(r1).max(), np.abs(r2).max())
+    for setting in (1, 2):
+        if setting == 1:
+            dq, dk = skl.streamkl_bwd_fixP1(d["q1"], d["k1"], d["q2"], d["k2"], l1, l2, d["g"],
+                                            causal=w.causal)
+        else:
+            dq, dk = skl.streamkl_bwd_fixP2(d["q1"], d["k1"], d["q2"], d["k2"], l1, l2, kl,
+                                            d["g"], causal=w.causal)
+        rdq, rdk = oracle.backward(setting, r["q1"], r["k1"], r["q2"], r["k2"], r["g"], w.scale,
+                                   w.causal)
+        # rows of opposite sign cancel in dK: the bf16 rounding of dS bounds that error
+        check_grads(w, r, setting, dq, dk, rdq, rdk, lmax,
+                    extra=bf16_ds_bound(setting, r, w.scale, w.causal))

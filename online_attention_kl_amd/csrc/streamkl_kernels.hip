@@ -73,6 +73,14 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
+// Waits until every global load of the wave has returned (s_waitcnt vmcnt(0); the expcnt and
+// lgkmcnt fields are left at their maxima, i.e. not waited on). Called once after the loads of
+// operands that stay in registers for a whole kernel: the compiler's wait placement merges a
+// loop's entry and back edges, and without this it keeps waiting, inside the loop, for those
+// long-finished loads by counting down the in-order load counter, which also waits for the
+// next tile's prefetch and so cuts its lead to a few hundred cycles.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Row (within a 32-row block) of accumulator register r of a 32x32 MFMA result for a lane in
 // half h (lanes 32..63 are h = 1). The lane's column is lane & 31.
 __device__ __forceinline__ int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
@@ -734,6 +742,7 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   const float b2 = -lse2[ro] * kLog2e;                                   // setting 1
   const float cst = SETTING == 2 ? (lse2[ro] - lse1[ro]) - klv[ro] : 0.f;  // setting 2
   if (h == 0) gscale[w][col] = gv[ro] * s.scale;
+  wait_global_loads();
 
   const int last_q = min(s.nq - 1, qb * BQ + BQ - 1);
   const int kend = CAUSAL ? min(s.nk, last_q + 1) : s.nk;
@@ -913,6 +922,7 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
     f1[kk] = load_frag(K1 + (long long)krow * s.k_sr + kk * 16 + h * 8);
     f2[kk] = SHARED_K ? f1[kk] : load_frag(K2 + (long long)krow * s.k_sr + kk * 16 + h * 8);
   }
+  wait_global_loads();
   const float c = s.scale * kLog2e;
   // query tiles run from the last one down to the first visible one, so that the blocks of one
   // slice, which start together, stream the same tiles at the same time
@@ -925,37 +935,41 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   for (int nb = 0; nb < NB; ++nb) dk[nb] = f32x16{};
 
   BwdStage<D, 2> st;
-  // constants of query tile row threadIdx.x (< kBT, lanes of wave 0) and the tile's sign flag
-  float cq0 = 0.f, cq1 = 0.f, cq2 = 0.f;
-  int cneg = 0;
+  // Per-query values of the prefetched tile, row threadIdx.x (< kBT, lanes of wave 0). They are
+  // only loaded here and turned into the tile's constants when the tile is staged, one tile of
+  // compute later, so that nothing waits for the loads in between.
+  float rx1 = 0.f, rx2 = 0.f, rg = 0.f, rkl = 0.f;
+  bool rvalid = false;
   auto load_tile = [&](int t) {
     st.load(Q1, Q2, s.q_sr, t * kBT, s.nq);
     if (threadIdx.x < kBT) {
       const int q = t * kBT + threadIdx.x;
-      // rows past n_q (and rows with g = 0) get P = 0: bias -inf
-      cq0 = -kInf;
-      cq1 = SETTING == 1 ? -kInf : 0.f;
-      cq2 = 1.f;
-      bool neg = false;
-      if (q < s.nq) {
-        const float x1 = lse1[rbase + q], x2 = lse2[rbase + q], g = gv[rbase + q];
-        const float lg = g != 0.f ? log2_hw(fabsf(g)) : -kInf;
-        cq0 = fmaf(-x1, kLog2e, lg);
-        cq1 = SETTING == 1 ? fmaf(-x2, kLog2e, lg) : (x2 - x1) - klv[rbase + q];
-        cq2 = g < 0.f ? -1.f : 1.f;
-        neg = g < 0.f;
+      rvalid = q < s.nq;
+      if (rvalid) {
+        rx1 = lse1[rbase + q];
+        rx2 = lse2[rbase + q];
+        rg = gv[rbase + q];
+        if (SETTING == 2) rkl = klv[rbase + q];
       }
-      cneg = __any(neg) ? 1 : 0;
     }
   };
   auto stage_store = [&](int buf) {
     uint16_t* base = lds + buf * BUF;
     st.store(base, base + L::RM, base + 2 * L::RM, FREE);
     if (threadIdx.x < kBT) {
+      // rows past n_q (and rows with g = 0) get P = 0: bias -inf
+      float cq0 = -kInf, cq1 = SETTING == 1 ? -kInf : 0.f, cq2 = 1.f;
+      if (rvalid) {
+        const float lg = rg != 0.f ? log2_hw(fabsf(rg)) : -kInf;
+        cq0 = fmaf(-rx1, kLog2e, lg);
+        cq1 = SETTING == 1 ? fmaf(-rx2, kLog2e, lg) : (rx2 - rx1) - rkl;
+        cq2 = rg < 0.f ? -1.f : 1.f;
+      }
+      const bool neg = __any(rvalid && rg < 0.f);
       qa[buf][0][threadIdx.x] = cq0;
       qa[buf][1][threadIdx.x] = cq1;
       qa[buf][2][threadIdx.x] = cq2;
-      if (threadIdx.x == 0) qneg[buf] = cneg;
+      if (threadIdx.x == 0) qneg[buf] = neg ? 1 : 0;
     }
   };
   const int ntiles = t_hi >= t_lo ? t_hi - t_lo + 1 : 0;

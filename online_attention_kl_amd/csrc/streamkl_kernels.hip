@@ -81,6 +81,17 @@ __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf
 // next tile's prefetch and so cuts its lead to a few hundred cycles.
 __device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// The flag unchanged, passed through a VGPR so that the compiler takes it for a per-lane value.
+// Used for the choice between the masked and unmasked dS variants in the backward kernels: when
+// the compiler can see that the choice is wave-uniform (non-causal instances), it lays the two
+// variants out so that their registers are live together and those instances spill; as a per-lane
+// condition (as in the causal instances) they fit. At run time the flag is uniform either way.
+__device__ __forceinline__ bool lane_flag(bool f) {
+  int v = f;
+  asm volatile("" : "+v"(v));
+  return v != 0;
+}
+
 // Row (within a 32-row block) of accumulator register r of a 32x32 MFMA result for a lane in
 // half h (lanes 32..63 are h = 1). The lane's column is lane & 31.
 __device__ __forceinline__ int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
@@ -829,7 +840,7 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
 #pragma unroll
       for (int rb = 0; rb < kBwdRB; ++rb) {
         const int kb0 = key0 + rb * 32;
-        if ((kb0 + 32 <= s.nk) && (!CAUSAL || kb0 + 31 <= qw0))
+        if (lane_flag((kb0 + 32 <= s.nk) && (!CAUSAL || kb0 + 31 <= qw0)))
           ds_block(std::false_type{}, rb);
         else
           ds_block(std::true_type{}, rb);
@@ -1060,7 +1071,7 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
 #pragma unroll
       for (int rb = 0; rb < kBwdRB; ++rb) {
         const int qb0 = qt0 + rb * 32;
-        const bool full = (qb0 + 32 <= s.nq) && (!CAUSAL || qb0 >= kw0 + 31);
+        const bool full = lane_flag((qb0 + 32 <= s.nq) && (!CAUSAL || qb0 >= kw0 + 31));
         // two variants only (a third costs registers): tiles that straddle the diagonal or
         // the ragged end, or hold a negative g, take the masked variant that applies the sign
         if (full && !signed_tile)

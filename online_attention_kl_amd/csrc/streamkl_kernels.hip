@@ -575,28 +575,50 @@ fwd_split_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
   }
 }
 
-// One thread per (slice, query row): merge the nsplit partial states and finish the row.
+// Merges the partial state (m, l) of one side and the side-1-weighted acc of another range
+// into the running one (running maxima; c converts a logit difference to a base-2 exponent).
+__device__ __forceinline__ void merge_partial(float& M1, float& L1, float& A, float& M2, float& L2,
+                                              float m1, float l1, float a, float m2, float l2,
+                                              float c) {
+  const float n1 = fmaxf(M1, m1), n2 = fmaxf(M2, m2);
+  const float fa = exp2_hw((M1 - n1) * c), fb = exp2_hw((m1 - n1) * c);
+  const float ga = exp2_hw((M2 - n2) * c), gb = exp2_hw((m2 - n2) * c);
+  L1 = fmaf(L1, fa, l1 * fb);
+  A = fmaf(A, fa, a * fb);
+  L2 = fmaf(L2, ga, l2 * gb);
+  M1 = n1;
+  M2 = n2;
+}
+
+// Merge of the nsplit partial states of each (slice, query row) and the row's outputs. A group of
+// `group` lanes (a power of two up to 64, inside one wavefront) serves one row: lane j merges
+// ranges j, j + group, ... in one pass, then the group combines its lanes' states by butterfly
+// exchanges. With few rows and many ranges the ranges are read in parallel instead of by one
+// thread in sequence.
 __global__ void __launch_bounds__(256)
 fwd_merge_kernel(const float* __restrict__ part, float* __restrict__ kl_out,
-                 float* __restrict__ lse1_out, float* __restrict__ lse2_out, Shape s, int nsplit) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)s.bh * s.nq) return;
-  const int slice = (int)(idx / s.nq), q = (int)(idx - (long long)slice * s.nq);
+                 float* __restrict__ lse1_out, float* __restrict__ lse2_out, Shape s, int nsplit,
+                 int group) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int lane = (int)(gid & (group - 1));
+  const long long idx = gid / group;
+  const long long rows = (long long)s.bh * s.nq;
+  // lanes of a row past the end still take part in the exchanges, on row 0, and write nothing
+  const long long row = idx < rows ? idx : 0;
+  const int slice = (int)(row / s.nq), q = (int)(row - (long long)slice * s.nq);
   const float c = s.scale * kLog2e;
   const float* p = part + (long long)slice * nsplit * 5 * s.nq + q;
-  float M1 = kNegBig, M2 = kNegBig;
-  for (int i = 0; i < nsplit; ++i) {
-    M1 = fmaxf(M1, p[(long long)(5 * i) * s.nq]);
-    M2 = fmaxf(M2, p[(long long)(5 * i + 2) * s.nq]);
-  }
-  float L1 = 0.f, L2 = 0.f, A = 0.f;
-  for (int i = 0; i < nsplit; ++i) {
+  float M1 = kNegBig, M2 = kNegBig, L1 = 0.f, L2 = 0.f, A = 0.f;
+  for (int i = lane; i < nsplit; i += group) {
     const float* pi = p + (long long)(5 * i) * s.nq;
-    const float e1 = exp2_hw((pi[0] - M1) * c), e2 = exp2_hw((pi[2 * s.nq] - M2) * c);
-    L1 = fmaf(pi[s.nq], e1, L1);
-    A = fmaf(pi[4 * s.nq], e1, A);
-    L2 = fmaf(pi[3 * s.nq], e2, L2);
+    merge_partial(M1, L1, A, M2, L2, pi[0], pi[s.nq], pi[4 * s.nq], pi[2 * s.nq], pi[3 * s.nq], c);
   }
+  for (int off = 1; off < group; off <<= 1) {
+    const float m1 = __shfl_xor(M1, off), l1 = __shfl_xor(L1, off), a = __shfl_xor(A, off);
+    const float m2 = __shfl_xor(M2, off), l2 = __shfl_xor(L2, off);
+    merge_partial(M1, L1, A, M2, L2, m1, l1, a, m2, l2, c);
+  }
+  if (idx >= rows || lane != 0) return;
   const float lse1 = M1 * s.scale + log2_hw(L1) * kLn2;
   const float lse2 = M2 * s.scale + log2_hw(L2) * kLn2;
   kl_out[idx] = s.scale * A / L1 + (lse2 - lse1);
@@ -1261,8 +1283,11 @@ void launch_fwd_split(const Shape& s, const SplitPlan& plan, const void* q1, con
                      (const uint16_t*)q2, (const uint16_t*)k2, part, s, plan.nsplit,
                      plan.split_keys);
   const long long rows = (long long)s.bh * s.nq;
-  hipLaunchKernelGGL(fwd_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
-                     (const float*)part, kl, l1, l2, s, plan.nsplit);
+  int group = 1;  // lanes per row in the merge: the ranges' count rounded up to a power of two
+  while (group < 64 && group < plan.nsplit) group *= 2;
+  const long long threads = rows * group;
+  hipLaunchKernelGGL(fwd_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     (const float*)part, kl, l1, l2, s, plan.nsplit, group);
 }
 
 template <int D, int SET, bool CAUSAL, bool SK>

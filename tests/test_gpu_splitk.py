@@ -46,7 +46,7 @@ def test_splitk_matches_oracle(shape, recipe):
     w, d, r = make(shape, recipe)
     rk, r1, r2 = oracle.forward(r["q1"], r["k1"], r["q2"], r["k2"], w.scale, w.causal)
     base = skl.streamkl_fwd(d["q1"], d["k1"], d["q2"], d["k2"], causal=w.causal)
-    for n_splits in (0, 1, 3, 1000):
+    for n_splits in (0, 1, 3, 64, 65, 1000):
         kl, l1, l2 = skl.streamkl_fwd_splitk(d["q1"], d["k1"], d["q2"], d["k2"], causal=w.causal,
                                              n_splits=n_splits)
         tag = f"n_splits={n_splits} "

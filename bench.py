@@ -163,9 +163,10 @@ def cpu_baseline(w, x, target_s: float):
 def small_nq(args):
     """Few query rows (decode-like), 32 heads, 64K keys, d=128, non-causal, backward setting 1:
     one JSON line per N_Q with the one-pass forward against the split-K forward and the
-    one-kernel dQ against the key-split dQ (dK alongside). The split-K forward reads every key
-    once, so its roofline is HBM bandwidth: algorithmic bytes = Q1, Q2, K1, K2 read once plus
-    KL, LSE1, LSE2 written, over the duration of the call (split kernel + merge kernel)."""
+    one-kernel dQ against the key-split dQ (dK alongside), and for N_Q <= 64 the fused backward
+    (one key-major pass for dQ and dK). The split-K forward reads every key once, so its
+    roofline is HBM bandwidth: algorithmic bytes = Q1, Q2, K1, K2 read once plus KL, LSE1, LSE2
+    written, over the duration of the call (split kernel + merge kernel)."""
     import numpy as np
     import torch
     import online_attention_kl_amd as skl
@@ -173,7 +174,7 @@ def small_nq(args):
 
     dev = torch.device("cuda:0")
     B, H, nk, d = 1, 32, 65536, 128
-    nqs = (1, 16, 128, 512)
+    nqs = (1, 16, 64, 128, 512)
     w = Workload("small_nq", B, H, max(nqs), nk, d, False, (1,), 5, "perturb", sigma=0.5)
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     x = make_inputs(w)
@@ -197,6 +198,10 @@ def small_nq(args):
         wsq = torch.empty(max(16, skl.streamkl_bwd_dq_splitk_workspace_size(q1, k1, 0)),
                           dtype=torch.uint8, device=dev)
         dq, dk = torch.empty_like(q2), torch.empty_like(k2)
+        fused = nq <= 64
+        if fused:
+            wsb = torch.empty(max(16, skl.streamkl_bwd_fused_workspace_size(q1, k1)),
+                              dtype=torch.uint8, device=dev)
         fns = {
             "fwd_one_pass": lambda: skl.streamkl_fwd(q1, k1, q2, k2, out=out),
             "fwd_split_k": lambda: skl.streamkl_fwd_splitk(q1, k1, q2, k2, workspace=wsf, out=out),
@@ -205,6 +210,9 @@ def small_nq(args):
                                                            workspace=wsq, out=dq),
             "dk": lambda: skl.streamkl_bwd_dk(1, q1, k1, q2, k2, l1, l2, kl, g, out=dk),
         }
+        if fused:
+            fns["bwd_fused"] = lambda: skl.streamkl_bwd_fused(1, q1, k1, q2, k2, l1, l2, None, g,
+                                                              workspace=wsb, out=(dq, dk))
         ms = {}
         for name, fn in fns.items():
             for _ in range(args.warmup):
@@ -229,7 +237,12 @@ def small_nq(args):
             "speedup": {"fwd": round(ms["fwd_one_pass"] / ms["fwd_split_k"], 2),
                         "dq": round(ms["dq_one_kernel"] / ms["dq_split"], 2),
                         "backward": round((ms["dq_one_kernel"] + ms["dk"]) /
-                                          (ms["dq_split"] + ms["dk"]), 2)},
+                                          (ms["dq_split"] + ms["dk"]), 2),
+                        "backward_fused_vs_split": (round((ms["dq_split"] + ms["dk"]) /
+                                                          ms["bwd_fused"], 2) if fused else None),
+                        "backward_fused_vs_one_kernel": (
+                            round((ms["dq_one_kernel"] + ms["dk"]) / ms["bwd_fused"], 2)
+                            if fused else None)},
             "roofline": {"kernel": "fwd_split_kernel + fwd_merge_kernel", "bound": "hbm",
                          "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
                          "frac": round(gbs / 8000.0, 4), "traffic": None},

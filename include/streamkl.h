@@ -224,6 +224,39 @@ streamkl_status_t streamkl_bwd_dq_splitk(const streamkl_problem_t* problem, int3
                                          int32_t n_splits, void* workspace,
                                          size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Fused backward for few query rows (n_q <= 64): the pages' fused single visit of the key
+ * tiles for small N_Q (gist.science/pt "Resumo Tecnico": "Metodologia" section 2, kernel fusion;
+ * "Resultados Experimentais", ablation: fused against separate backward kernels for small N_Q).
+ * One key-major pass recomputes S1 and S2 per (query tile, 32-key group), forms dS of the
+ * setting's free side once, and uses it for both products: dK of the group's keys is written
+ * directly, and the block's partial dQ (its 128 * G keys) goes to the workspace; a second kernel sums
+ * the key blocks' partials in a fixed order and rounds once to bfloat16. The keys are read once
+ * instead of once per gradient. No atomics on global memory: the result is deterministic and
+ * agrees with streamkl_bwd_fixP1 / _fixP2 to float32 summation order before the rounding.
+ *
+ * setting: 1 (P1 fixed; outputs dQ2, dK2, kl unused and may be NULL) or 2 (P2 fixed; outputs
+ *   dQ1, dK1, kl required).
+ * dq, dk: contiguous bfloat16 [batch, heads, n_q, head_dim] and [batch, heads, n_k, head_dim].
+ * workspace: at least streamkl_bwd_fused_workspace_size(problem) bytes of device memory,
+ *   16-byte aligned, owned by the caller, overlapping no input or output; contents on entry
+ *   ignored, on return unspecified. It holds float32 [ceil(n_k / (128 G))][batch * heads][n_q]
+ *   [head_dim], where G, the 32-key groups per wave, is floor(S * batch * heads / 512) clamped to
+ *   [1, min(64, S)] with S = ceil(n_k / 128) (about two blocks per CU).
+ * Errors: as streamkl_bwd_fixP1 / _fixP2; STREAMKL_ERROR_NOT_SUPPORTED for n_q > 64;
+ * STREAMKL_ERROR_INVALID_VALUE for a bad setting or a too small, misaligned or overlapping
+ * workspace.
+ */
+/* Workspace bytes streamkl_bwd_fused needs (0 for a NULL problem, sizes < 1, n_q > 64 or an
+ * unsupported head_dim). */
+size_t streamkl_bwd_fused_workspace_size(const streamkl_problem_t* problem);
+streamkl_status_t streamkl_bwd_fused(const streamkl_problem_t* problem, int32_t setting,
+                                     const void* q1, const void* k1, const void* q2,
+                                     const void* k2, const float* lse1, const float* lse2,
+                                     const float* kl, const float* grad_kl, void* dq, void* dk,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* streamkl_status_string(streamkl_status_t status);
 

@@ -33,6 +33,7 @@ EXPORTS = ("streamkl_fwd", "streamkl_fwd_fp8", "streamkl_fwd_splitk", "streamkl_
            "streamkl_fwd_splitk_workspace_size", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2",
            "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_bwd_dq_splitk",
            "streamkl_bwd_dq_splitk_default_splits", "streamkl_bwd_dq_splitk_workspace_size",
+           "streamkl_bwd_fused", "streamkl_bwd_fused_workspace_size",
            "streamkl_status_string", "streamkl_last_error")
 
 
@@ -85,8 +86,12 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.streamkl_bwd_dq_splitk_default_splits.restype = ctypes.c_int32
     L.streamkl_bwd_dq_splitk_workspace_size.argtypes = [pp, ctypes.c_int32]
     L.streamkl_bwd_dq_splitk_workspace_size.restype = ctypes.c_size_t
+    L.streamkl_bwd_fused.argtypes = [pp, ctypes.c_int32, vp, vp, vp, vp, fp, fp, fp, fp, vp, vp,
+                                     vp, ctypes.c_size_t, vp]
+    L.streamkl_bwd_fused_workspace_size.argtypes = [pp]
+    L.streamkl_bwd_fused_workspace_size.restype = ctypes.c_size_t
     for name in ("streamkl_fwd", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2", "streamkl_bwd_dq",
-                 "streamkl_bwd_dk", "streamkl_bwd_dq_splitk"):
+                 "streamkl_bwd_dk", "streamkl_bwd_dq_splitk", "streamkl_bwd_fused"):
         getattr(L, name).restype = ctypes.c_int
     L.streamkl_status_string.argtypes = [ctypes.c_int]
     L.streamkl_status_string.restype = ctypes.c_char_p
@@ -340,4 +345,45 @@ def streamkl_bwd_dq_splitk(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, sca
                                         lse2.data_ptr(), kl.data_ptr() if kl is not None else None,
                                         grad_kl.data_ptr(), out.data_ptr(), int(n_splits),
                                         workspace.data_ptr(), nbytes, _stream(q1)))
+    return out
+
+
+def streamkl_bwd_fused_workspace_size(q1, k1, scale=None, causal=False) -> int:
+    p = make_problem(q1, k1, scale, causal)
+    return int(lib().streamkl_bwd_fused_workspace_size(ctypes.byref(p)))
+
+
+def streamkl_bwd_fused(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=None,
+                       causal=False, workspace=None, out=None):
+    """(dQ, dK) of the free side from one key-major pass (n_q <= 64); the workspace (a uint8
+    CUDA tensor of at least streamkl_bwd_fused_workspace_size bytes) is allocated here when
+    not given."""
+    import torch
+    _check_inputs(q1, k1, q2, k2)
+    B, H, nq, _ = q1.shape
+    vecs = [("lse1", lse1), ("lse2", lse2), ("grad_kl", grad_kl)]
+    if setting == 2:
+        vecs.append(("kl", kl))
+    for n, t in vecs:
+        _rowvec(t, n, (B, H, nq))
+    qf, kf = (q2, k2) if setting == 1 else (q1, k1)
+    if out is None:
+        out = (torch.empty(qf.shape, dtype=torch.bfloat16, device=qf.device),
+               torch.empty(kf.shape, dtype=torch.bfloat16, device=kf.device))
+    for t, ref, name in ((out[0], qf, "dq"), (out[1], kf, "dk")):
+        if t.dtype != torch.bfloat16 or t.shape != ref.shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor of shape "
+                             f"{tuple(ref.shape)}")
+    p = make_problem(q1, k1, scale, causal)
+    need = int(lib().streamkl_bwd_fused_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().streamkl_bwd_fused(ctypes.byref(p), setting, q1.data_ptr(), k1.data_ptr(),
+                                    q2.data_ptr(), k2.data_ptr(), lse1.data_ptr(),
+                                    lse2.data_ptr(), kl.data_ptr() if kl is not None else None,
+                                    grad_kl.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
+                                    workspace.data_ptr(), nbytes, _stream(q1)))
     return out

@@ -1121,6 +1121,245 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   }
 }
 
+// ---------------------------------------------------------------- fused backward (few queries)
+// For few query rows one key-major pass gives dK of the free side and, from the same dS tiles,
+// each key block's partial dQ, so that the keys are read once instead of once per gradient. All
+// query rows stay in LDS (Q1 and Q2 row-major, the free side also transposed); each wave walks
+// `groups` groups of 32 keys (a block covers groups * 128 consecutive keys, so that the staging of
+// the query rows and the block's dQ partial are paid once per many keys). The dQ product needs
+// dS with queries as rows, so each tile's dS goes
+// through a per-wave LDS scratch, and the wave's free-side keys are kept transposed in LDS as
+// that product's other operand. The block's partial dQ (already times scale) goes to
+// part[key block][slice][n_q][D]; dq_reduce_kernel sums the key blocks in a fixed order.
+constexpr int kFusedWaves = 4;  // one wave per SIMD: room for the dQ accumulators
+constexpr int kFusedThreads = 64 * kFusedWaves;
+constexpr int kFusedStep = 32 * kFusedWaves;  // keys of one step of the block's waves
+constexpr int kFusedMaxGroups = 64;           // 32-key groups per wave, at most
+constexpr int kFusedMaxQ = 64;                // query rows the fused path takes
+constexpr int kDsPitch = 32 + 8;                             // pitch (elements) of the dS scratch
+
+// Row `row` (columns col0..col0 + 7) of a tile into its transposed copy: element (row, col0 + j)
+// goes to transposed row col0 + j at position `pos`, as 16-bit stores.
+__device__ __forceinline__ void store_transposed8(uint16_t* tr, int pos, int col0, uint4 v) {
+  const unsigned w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    tr[(col0 + 2 * j) * kTPitch + pos] = (uint16_t)(w4[j] & 0xFFFFu);
+    tr[(col0 + 2 * j + 1) * kTPitch + pos] = (uint16_t)(w4[j] >> 16);
+  }
+}
+
+template <int D, int SETTING, bool CAUSAL, bool SHARED_K>
+__global__ void __launch_bounds__(kFusedThreads, 1)
+fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
+                 const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
+                 const float* __restrict__ lse1, const float* __restrict__ lse2,
+                 const float* __restrict__ klv, const float* __restrict__ gv,
+                 __bf16* __restrict__ dk_out, float* __restrict__ part, Shape s, int groups) {
+  constexpr int KS = D / 16, NB = D / 32, P = lds_pitch<D>(), CPR = D / 8;
+  constexpr int NQT = kFusedMaxQ / 32;
+  constexpr int FREE = 2 - SETTING;  // tensor index of the free side (1 = side 2)
+  __shared__ __attribute__((aligned(16))) uint16_t qrm[2][kFusedMaxQ * P];
+  __shared__ __attribute__((aligned(16))) uint16_t qtr[NQT][D * kTPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t ktr[kFusedWaves][D * kTPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t dsq[kFusedWaves][32 * kDsPitch];
+  __shared__ __attribute__((aligned(16))) float qa[3][kFusedMaxQ];
+  __shared__ __attribute__((aligned(16))) float dqacc[kFusedMaxQ * D];
+  __shared__ int qneg;
+
+  int kb, slice;
+  block_coords(s.bh, kb, slice);
+  const int b = slice / s.heads, hd = slice - b * s.heads;
+  const uint16_t* Q1 = q1 + b * s.q_sb + hd * s.q_sh;
+  const uint16_t* Q2 = q2 + b * s.q_sb + hd * s.q_sh;
+  const uint16_t* K1 = k1 + b * s.k_sb + hd * s.k_sh;
+  const uint16_t* K2 = k2 + b * s.k_sb + hd * s.k_sh;
+  const long long rbase = (long long)slice * s.nq;
+  const int l = lane_id(), w = wave_id(), h = l >> 5, col = l & 31;
+  const int nqt = (s.nq + 31) / 32;
+
+  // every query row: Q1 and Q2 row-major (rows past n_q zero), the free side also transposed
+  // (position tpos(row) of its 32-row tile, the order of a dS accumulator's rows)
+  for (int idx = threadIdx.x; idx < 2 * kFusedMaxQ * CPR; idx += kFusedThreads) {
+    const int te = idx / (kFusedMaxQ * CPR);
+    const int rem = idx - te * (kFusedMaxQ * CPR);
+    const int row = rem % kFusedMaxQ, chunk = rem / kFusedMaxQ;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < s.nq)
+      v = *reinterpret_cast<const uint4*>((te ? Q2 : Q1) + row * s.q_sr + chunk * 8);
+    *reinterpret_cast<uint4*>(&qrm[te][row * P + chunk * 8]) = v;
+    if (te == FREE) store_transposed8(qtr[row / 32], tpos(row % 32), chunk * 8, v);
+  }
+  // per query: exponent biases with log2 |g| folded in and sign(g), as in the dK kernel
+  if (threadIdx.x < kFusedMaxQ) {
+    const int q = threadIdx.x;
+    float cq0 = -kInf, cq1 = SETTING == 1 ? -kInf : 0.f, cq2 = 1.f;
+    bool neg = false;
+    if (q < s.nq) {
+      const float x1 = lse1[rbase + q], x2 = lse2[rbase + q], g = gv[rbase + q];
+      const float lg = g != 0.f ? log2_hw(fabsf(g)) : -kInf;
+      cq0 = fmaf(-x1, kLog2e, lg);
+      cq1 = SETTING == 1 ? fmaf(-x2, kLog2e, lg) : (x2 - x1) - klv[rbase + q];
+      cq2 = g < 0.f ? -1.f : 1.f;
+      neg = g < 0.f;
+    }
+    qa[0][q] = cq0;
+    qa[1][q] = cq1;
+    qa[2][q] = cq2;
+    const bool any_neg = __any(neg);
+    if (q == 0) qneg = any_neg ? 1 : 0;
+  }
+  for (int i = threadIdx.x; i < kFusedMaxQ * D; i += kFusedThreads) dqacc[i] = 0.f;
+  __syncthreads();
+  const bool signed_q = qneg != 0;
+  const float c = s.scale * kLog2e;
+
+  f32x16 pq[NQT][NB];  // this wave's partial dQ, queries as rows
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) pq[qt][nb] = f32x16{};
+
+  // S operands of one 32-key group of this wave (rows past n_k read the last key; their dS is
+  // masked), fetched one group ahead of their use
+  auto fetch = [&](int grp, bf16x8* a1, bf16x8* a2) {
+    const int key = (kb * groups + grp) * kFusedStep + w * 32 + col;
+    const long long ro = (long long)(key < s.nk ? key : s.nk - 1) * s.k_sr;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      a1[kk] = load_frag(K1 + ro + kk * 16 + h * 8);
+      a2[kk] = SHARED_K ? a1[kk] : load_frag(K2 + ro + kk * 16 + h * 8);
+    }
+  };
+  bf16x8 f1[KS], f2[KS];
+  fetch(0, f1, f2);
+  for (int grp = 0; grp < groups; ++grp) {
+    const int kw0 = (kb * groups + grp) * kFusedStep + w * 32;
+    if (kw0 >= s.nk) break;  // later groups lie further on
+    const int key = kw0 + col;
+    // the group's free-side keys transposed (head_dim as rows, keys in natural order), from
+    // the S operands: lane (key, h) holds head_dim kk * 16 + h * 8 .. + 7 of step kk
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      store_transposed8(ktr[w], col, kk * 16 + h * 8,
+                        __builtin_bit_cast(uint4, FREE ? f2[kk] : f1[kk]));
+    bf16x8 n1[KS], n2[KS];
+    fetch(grp + 1 < groups ? grp + 1 : grp, n1, n2);  // unconditional: counted waits
+    const bool ragged = kw0 + 32 > s.nk;
+    f32x16 dk[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) dk[nb] = f32x16{};
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int qt0 = qt * 32;
+      if (qt >= nqt || (CAUSAL && qt0 + 31 < kw0)) continue;
+      const uint16_t* qt1 = qrm[0] + qt0 * P;
+      const uint16_t* qt2 = qrm[1] + qt0 * P;
+      f32x16 x1 = f32x16{}, x2 = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        x1 = mfma(lds_a_frag<D>(qt1, col, kk, h), f1[kk], x1);
+        x2 = mfma(lds_a_frag<D>(qt2, col, kk, h), f2[kk], x2);
+      }
+      // dS^T with g folded in (masked variant: queries past n_q, keys past n_k, the causal
+      // diagonal, and the sign of g), its dK product, and dS stored with queries as rows
+      auto ds_tile = [&](auto maskc) {
+        constexpr bool MASK = decltype(maskc)::value;
+        float ds[16];
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int qi = qt0 + rq * 8 + h * 4;
+          const float4 va0 = *reinterpret_cast<const float4*>(&qa[0][qi]);
+          const float4 va1 = *reinterpret_cast<const float4*>(&qa[1][qi]);
+          const float4 va2 = MASK ? *reinterpret_cast<const float4*>(&qa[2][qi])
+                                  : make_float4(1.f, 1.f, 1.f, 1.f);
+          const float c0[4] = {va0.x, va0.y, va0.z, va0.w};
+          const float c1[4] = {va1.x, va1.y, va1.z, va1.w};
+          const float cs[4] = {va2.x, va2.y, va2.z, va2.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = rq * 4 + j;
+            float e1 = x1[r], e2 = x2[r];
+            const float d12 = e1 - e2;
+            if (MASK) {
+              const int q = qi + j;
+              const bool ok = q < s.nq && key < s.nk && (!CAUSAL || key <= q);
+              e1 = ok ? e1 : -kInf;
+              e2 = ok ? e2 : -kInf;
+            }
+            const float p1 = exp2_hw(fmaf(e1, c, c0[j]));
+            float v;
+            if (SETTING == 1)
+              v = exp2_hw(fmaf(e2, c, c1[j])) - p1;
+            else
+              v = p1 * fmaf(d12, s.scale, c1[j]);
+            ds[r] = MASK ? cs[j] * v : v;
+          }
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const bf16x8 a = pack8(ds + 8 * cc);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            dk[nb] = mfma(a, tr_frag(qtr[qt], nb, cc, col, h), dk[nb]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          dsq[w][acc_row(r, h) * kDsPitch + col] =
+              __builtin_bit_cast(uint16_t, static_cast<__bf16>(ds[r]));
+      };
+      if (lane_flag((qt0 + 32 <= s.nq) && !ragged && !signed_q && (!CAUSAL || qt0 >= kw0 + 31)))
+        ds_tile(std::false_type{});
+      else
+        ds_tile(std::true_type{});
+      // partial dQ of the tile over the group's keys: dS (queries as rows) times K_free
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const bf16x8 a = load_frag(&dsq[w][col * kDsPitch + cc * 16 + h * 8]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          pq[qt][nb] = mfma(a, tr_frag(ktr[w], nb, cc, col, h), pq[qt][nb]);
+      }
+    }
+    // dK rows of the group's keys
+    const long long obase = (long long)slice * s.nk;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = kw0 + acc_row(r, h);
+      if (kr < s.nk) {
+        __bf16* dst = dk_out + (obase + kr) * D + col;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) dst[nb * 32] = static_cast<__bf16>(dk[nb][r] * s.scale);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      f1[kk] = n1[kk];
+      f2[kk] = n2[kk];
+    }
+  }
+  // the block's partial dQ: the waves' accumulators summed in LDS, then written times scale
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    if (qt >= nqt) continue;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        atomicAdd(&dqacc[(qt * 32 + acc_row(r, h)) * D + nb * 32 + col], pq[qt][nb][r]);
+  }
+  __syncthreads();
+  float* dst = part + ((long long)kb * s.bh + slice) * s.nq * D;
+  for (int i = threadIdx.x * 4; i < s.nq * D; i += kFusedThreads * 4) {
+    float4 v = *reinterpret_cast<const float4*>(&dqacc[i]);
+    v.x *= s.scale;
+    v.y *= s.scale;
+    v.z *= s.scale;
+    v.w *= s.scale;
+    *reinterpret_cast<float4*>(dst + i) = v;
+  }
+}
+
 // ================================================================ host side
 thread_local std::string g_last_error;
 
@@ -1385,12 +1624,63 @@ void dispatch_bwd(int64_t d, bool causal, bool sk, const Shape& s, const void* q
 #undef SKL_BWD
 }
 
+// Key groups per wave of the fused backward: as many as keep about two blocks per CU (512
+// blocks), between 1 and kFusedMaxGroups.
+int fused_groups(const streamkl_problem_t* p) {
+  const int64_t steps = (p->n_k + kFusedStep - 1) / kFusedStep;  // per slice
+  int64_t g = steps * p->batch * p->heads / 512;
+  if (g > kFusedMaxGroups) g = kFusedMaxGroups;
+  if (g > steps) g = steps;
+  return g < 1 ? 1 : (int)g;
+}
+
+int64_t fused_key_blocks(const streamkl_problem_t* p) {
+  const int64_t keys = (int64_t)kFusedStep * fused_groups(p);
+  return (p->n_k + keys - 1) / keys;
+}
+
+size_t fused_workspace_bytes(const streamkl_problem_t* p) {
+  return (size_t)fused_key_blocks(p) * p->batch * p->heads * p->n_q * p->head_dim * sizeof(float);
+}
+
+template <int D, int SET, bool CAUSAL, bool SK>
+void launch_fused(const Shape& s, int groups, const void* q1, const void* k1, const void* q2,
+                  const void* k2, const float* l1, const float* l2, const float* kl,
+                  const float* g, void* dq, void* dk, float* part, hipStream_t st) {
+  const int nkb = (s.nk + kFusedStep * groups - 1) / (kFusedStep * groups);
+  hipLaunchKernelGGL((fused_bwd_kernel<D, SET, CAUSAL, SK>), dim3(nkb * s.bh),
+                     dim3(kFusedThreads), 0, st, (const uint16_t*)q1, (const uint16_t*)k1,
+                     (const uint16_t*)q2, (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dk, part,
+                     s, groups);
+  const long long n4 = (long long)s.bh * s.nq * D / 4;
+  hipLaunchKernelGGL(dq_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                     (const float*)part, (__bf16*)dq, n4, nkb);
+}
+
+template <int SET>
+void dispatch_fused(int64_t d, bool causal, bool sk, const Shape& s, int groups, const void* q1,
+                    const void* k1, const void* q2, const void* k2, const float* l1,
+                    const float* l2, const float* kl, const float* g, void* dq, void* dk,
+                    float* part, hipStream_t st) {
+#define SKL_FUS(DD, C, S) \
+  launch_fused<DD, SET, C, S>(s, groups, q1, k1, q2, k2, l1, l2, kl, g, dq, dk, part, st)
+  if (d == 64) {
+    if (causal) { if (sk) SKL_FUS(64, true, true); else SKL_FUS(64, true, false); }
+    else { if (sk) SKL_FUS(64, false, true); else SKL_FUS(64, false, false); }
+  } else {
+    if (causal) { if (sk) SKL_FUS(128, true, true); else SKL_FUS(128, true, false); }
+    else { if (sk) SKL_FUS(128, false, true); else SKL_FUS(128, false, false); }
+  }
+#undef SKL_FUS
+}
+
 streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const void* q1,
                              const void* k1, const void* q2, const void* k2, const float* lse1,
                              const float* lse2, const float* kl, const float* grad_kl, void* dq,
                              void* dk, bool want_dq, bool want_dk, hipStream_t stream,
                              const char* what, const int32_t* dq_splits = nullptr,
-                             void* workspace = nullptr, size_t workspace_bytes = 0) {
+                             void* workspace = nullptr, size_t workspace_bytes = 0,
+                             bool fused = false) {
   Shape s;
   streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
   if (st != STREAMKL_SUCCESS) return st;
@@ -1398,9 +1688,12 @@ streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const voi
   if (!lse1 || !lse2 || !grad_kl || (setting == 2 && !kl))
     return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": NULL lse / kl / grad pointer");
   const int64_t n = p->batch * p->heads * p->n_q;
+  if (fused && p->n_q > kFusedMaxQ)
+    return fail(STREAMKL_ERROR_NOT_SUPPORTED,
+                std::string(what) + ": n_q must be at most " + std::to_string(kFusedMaxQ));
   DqSplitPlan plan = {1, 0};
   if (dq_splits) plan = dq_split_plan(p, *dq_splits);
-  const size_t need = dq_split_workspace_bytes(p, plan.nsplit);
+  const size_t need = fused ? fused_workspace_bytes(p) : dq_split_workspace_bytes(p, plan.nsplit);
   if (workspace_bytes < need)
     return fail(STREAMKL_ERROR_INVALID_VALUE,
                 std::string(what) + ": workspace too small (" + std::to_string(workspace_bytes) +
@@ -1420,9 +1713,21 @@ streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const voi
   if (plan.nsplit > 1 &&
       (int64_t)plan.nsplit * p->batch * p->heads * ((p->n_q + 255) / 256) >= ((int64_t)1 << 31))
     return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": grid too large");
+  if (fused && fused_key_blocks(p) * p->batch * p->heads >= ((int64_t)1 << 31))
+    return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": grid too large");
   (void)hipGetLastError();
   void* dqp = want_dq ? dq : nullptr;
   void* dkp = want_dk ? dk : nullptr;
+  if (fused) {
+    float* part = static_cast<float*>(workspace);
+    if (setting == 1)
+      dispatch_fused<1>(p->head_dim, p->causal != 0, k1 == k2, s, fused_groups(p), q1, k1, q2,
+                        k2, lse1, lse2, nullptr, grad_kl, dq, dk, part, stream);
+    else
+      dispatch_fused<2>(p->head_dim, p->causal != 0, k1 == k2, s, fused_groups(p), q1, k1, q2,
+                        k2, lse1, lse2, kl, grad_kl, dq, dk, part, stream);
+    return check_launch(what);
+  }
   if (dqp && plan.nsplit > 1) {
     float* part = static_cast<float*>(workspace);
     if (setting == 1)
@@ -1581,6 +1886,22 @@ streamkl_status_t streamkl_bwd_dq_splitk(const streamkl_problem_t* p, int32_t se
                                          size_t workspace_bytes, hipStream_t stream) {
   return bwd_common(p, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, dq, nullptr, true, false,
                     stream, "streamkl_bwd_dq_splitk", &n_splits, workspace, workspace_bytes);
+}
+
+size_t streamkl_bwd_fused_workspace_size(const streamkl_problem_t* p) {
+  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1 || p->n_q > kFusedMaxQ ||
+      (p->head_dim != 64 && p->head_dim != 128))
+    return 0;
+  return fused_workspace_bytes(p);
+}
+
+streamkl_status_t streamkl_bwd_fused(const streamkl_problem_t* p, int32_t setting, const void* q1,
+                                     const void* k1, const void* q2, const void* k2,
+                                     const float* lse1, const float* lse2, const float* kl,
+                                     const float* grad_kl, void* dq, void* dk, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common(p, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, dq, dk, true, true,
+                    stream, "streamkl_bwd_fused", nullptr, workspace, workspace_bytes, true);
 }
 
 const char* streamkl_status_string(streamkl_status_t status) {

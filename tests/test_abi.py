@@ -191,3 +191,37 @@ def test_dq_splitk_invalid_workspace():
     assert call(K1 + 64, need) == 1 and "overlap" in last_error()
     # one range: no workspace needed, validation passes up to the launch (no GPU here)
     assert L.streamkl_bwd_dq_splitk_workspace_size(ctypes.byref(p), 1) == 0
+
+
+def test_fused_workspace_and_limits():
+    L = skl.lib()
+    assert L.streamkl_bwd_fused_workspace_size(None) == 0
+    for nq, nk, d, heads in ((1, 65536, 128, 32), (64, 80, 128, 2), (17, 513, 64, 2),
+                             (64, 1, 64, 2), (3, 4096, 128, 32), (5, 300000, 64, 8)):
+        p = good_problem(d)
+        p.n_q, p.n_k, p.heads = nq, nk, heads
+        steps = -(-nk // 128)
+        groups = max(1, min(64, steps, steps * heads // 512))
+        nkb = -(-nk // (128 * groups))
+        assert L.streamkl_bwd_fused_workspace_size(ctypes.byref(p)) == nkb * heads * nq * d * 4
+    p = good_problem()
+    p.n_q = 65
+    assert L.streamkl_bwd_fused_workspace_size(ctypes.byref(p)) == 0
+    WS = 0x7A000000
+
+    def call(p, setting=1, ws=WS, nbytes=1 << 30):
+        return L.streamkl_bwd_fused(ctypes.byref(p), setting, Q1, K1, Q2, K2, O1, O2, O3,
+                                    0x7C000000, 0x7D000000, 0x7E000000, ws, nbytes, None)
+    # n_q past the fused path's limit: valid but not supported
+    assert call(p) == 2 and "n_q" in last_error()
+    p = good_problem()
+    need = L.streamkl_bwd_fused_workspace_size(ctypes.byref(p))
+    assert call(p, nbytes=need - 4) == 1 and "workspace too small" in last_error()
+    assert call(p, ws=0, nbytes=need) == 1
+    assert call(p, ws=WS + 8, nbytes=need) == 1 and "aligned" in last_error()
+    assert call(p, ws=K1 + 64, nbytes=need) == 1 and "overlap" in last_error()
+    assert call(p, setting=3, nbytes=need) == 1
+    # setting 2 needs kl
+    r = L.streamkl_bwd_fused(ctypes.byref(p), 2, Q1, K1, Q2, K2, O1, O2, None, 0x7C000000,
+                             0x7D000000, 0x7E000000, WS, need, None)
+    assert r == 1

@@ -1149,7 +1149,8 @@ __device__ __forceinline__ void store_transposed8(uint16_t* tr, int pos, int col
   }
 }
 
-template <int D, int SETTING, bool CAUSAL, bool SHARED_K>
+// NQT: 32-row query tiles held (1 for n_q <= 32, else 2); fewer tiles, fewer registers and LDS.
+template <int D, int SETTING, bool CAUSAL, bool SHARED_K, int NQT>
 __global__ void __launch_bounds__(kFusedThreads, 1)
 fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
                  const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
@@ -1157,14 +1158,14 @@ fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
                  const float* __restrict__ klv, const float* __restrict__ gv,
                  __bf16* __restrict__ dk_out, float* __restrict__ part, Shape s, int groups) {
   constexpr int KS = D / 16, NB = D / 32, P = lds_pitch<D>(), CPR = D / 8;
-  constexpr int NQT = kFusedMaxQ / 32;
+  constexpr int MQ = 32 * NQT;  // query rows held
   constexpr int FREE = 2 - SETTING;  // tensor index of the free side (1 = side 2)
-  __shared__ __attribute__((aligned(16))) uint16_t qrm[2][kFusedMaxQ * P];
+  __shared__ __attribute__((aligned(16))) uint16_t qrm[2][MQ * P];
   __shared__ __attribute__((aligned(16))) uint16_t qtr[NQT][D * kTPitch];
   __shared__ __attribute__((aligned(16))) uint16_t ktr[kFusedWaves][D * kTPitch];
   __shared__ __attribute__((aligned(16))) uint16_t dsq[kFusedWaves][32 * kDsPitch];
-  __shared__ __attribute__((aligned(16))) float qa[3][kFusedMaxQ];
-  __shared__ __attribute__((aligned(16))) float dqacc[kFusedMaxQ * D];
+  __shared__ __attribute__((aligned(16))) float qa[3][MQ];
+  __shared__ __attribute__((aligned(16))) float dqacc[MQ * D];
   __shared__ int qneg;
 
   int kb, slice;
@@ -1180,10 +1181,10 @@ fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
 
   // every query row: Q1 and Q2 row-major (rows past n_q zero), the free side also transposed
   // (position tpos(row) of its 32-row tile, the order of a dS accumulator's rows)
-  for (int idx = threadIdx.x; idx < 2 * kFusedMaxQ * CPR; idx += kFusedThreads) {
-    const int te = idx / (kFusedMaxQ * CPR);
-    const int rem = idx - te * (kFusedMaxQ * CPR);
-    const int row = rem % kFusedMaxQ, chunk = rem / kFusedMaxQ;
+  for (int idx = threadIdx.x; idx < 2 * MQ * CPR; idx += kFusedThreads) {
+    const int te = idx / (MQ * CPR);
+    const int rem = idx - te * (MQ * CPR);
+    const int row = rem % MQ, chunk = rem / MQ;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (row < s.nq)
       v = *reinterpret_cast<const uint4*>((te ? Q2 : Q1) + row * s.q_sr + chunk * 8);
@@ -1191,7 +1192,7 @@ fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
     if (te == FREE) store_transposed8(qtr[row / 32], tpos(row % 32), chunk * 8, v);
   }
   // per query: exponent biases with log2 |g| folded in and sign(g), as in the dK kernel
-  if (threadIdx.x < kFusedMaxQ) {
+  if (threadIdx.x < MQ) {
     const int q = threadIdx.x;
     float cq0 = -kInf, cq1 = SETTING == 1 ? -kInf : 0.f, cq2 = 1.f;
     bool neg = false;
@@ -1209,7 +1210,7 @@ fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
     const bool any_neg = __any(neg);
     if (q == 0) qneg = any_neg ? 1 : 0;
   }
-  for (int i = threadIdx.x; i < kFusedMaxQ * D; i += kFusedThreads) dqacc[i] = 0.f;
+  for (int i = threadIdx.x; i < MQ * D; i += kFusedThreads) dqacc[i] = 0.f;
   __syncthreads();
   const bool signed_q = qneg != 0;
   const float c = s.scale * kLog2e;
@@ -1648,10 +1649,16 @@ void launch_fused(const Shape& s, int groups, const void* q1, const void* k1, co
                   const void* k2, const float* l1, const float* l2, const float* kl,
                   const float* g, void* dq, void* dk, float* part, hipStream_t st) {
   const int nkb = (s.nk + kFusedStep * groups - 1) / (kFusedStep * groups);
-  hipLaunchKernelGGL((fused_bwd_kernel<D, SET, CAUSAL, SK>), dim3(nkb * s.bh),
-                     dim3(kFusedThreads), 0, st, (const uint16_t*)q1, (const uint16_t*)k1,
-                     (const uint16_t*)q2, (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dk, part,
-                     s, groups);
+  if (s.nq <= 32)
+    hipLaunchKernelGGL((fused_bwd_kernel<D, SET, CAUSAL, SK, 1>), dim3(nkb * s.bh),
+                       dim3(kFusedThreads), 0, st, (const uint16_t*)q1, (const uint16_t*)k1,
+                       (const uint16_t*)q2, (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dk,
+                       part, s, groups);
+  else
+    hipLaunchKernelGGL((fused_bwd_kernel<D, SET, CAUSAL, SK, 2>), dim3(nkb * s.bh),
+                       dim3(kFusedThreads), 0, st, (const uint16_t*)q1, (const uint16_t*)k1,
+                       (const uint16_t*)q2, (const uint16_t*)k2, l1, l2, kl, g, (__bf16*)dk,
+                       part, s, groups);
   const long long n4 = (long long)s.bh * s.nq * D / 4;
   hipLaunchKernelGGL(dq_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
                      (const float*)part, (__bf16*)dq, n4, nkb);

@@ -35,9 +35,15 @@
 //    the diagonal or the ragged end of a sequence take the masked path. Causal grids run the
 //    longest row blocks first, and block ids interleave the (batch, head) slices so that all
 //    blocks of one slice land on one XCD and share its L2.
+//  * The dK kernel folds the upstream gradient into the exponents (g P = sign(g) 2^(y + log2|g|))
+//    and applies the sign only on tiles that hold a negative g.
 //  * Few query rows: a split-K forward (one wavefront per query block and key range, partial
-//    states merged by a second kernel) and a dQ kernel split over key ranges with a
-//    deterministic sum of the partials; both take a workspace from the caller.
+//    states merged by a lane group per row), a dQ kernel split over key ranges with a
+//    deterministic sum of the partials, and a fused backward (n_q <= 64) that forms dS once per
+//    key group and uses it for dK and for a per-block partial dQ, reading the keys once; all
+//    three take a workspace from the caller.
+//  * The forward is also built for fp8 e4m3 inputs (v_mfma_scale_f32_32x32x64_f8f6f4, one
+//    dequantisation factor per side), with the same float32 state.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

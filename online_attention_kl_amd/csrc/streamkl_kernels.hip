@@ -1228,7 +1228,7 @@ fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
     for (int nb = 0; nb < NB; ++nb) pq[qt][nb] = f32x16{};
 
   // S operands of one 32-key group of this wave (rows past n_k read the last key; their dS is
-  // masked), fetched one group ahead of their use
+  // masked)
   auto fetch = [&](int grp, bf16x8* a1, bf16x8* a2) {
     const int key = (kb * groups + grp) * kFusedStep + w * 32 + col;
     const long long ro = (long long)(key < s.nk ? key : s.nk - 1) * s.k_sr;
@@ -1250,8 +1250,11 @@ fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
     for (int kk = 0; kk < KS; ++kk)
       store_transposed8(ktr[w], col, kk * 16 + h * 8,
                         __builtin_bit_cast(uint4, FREE ? f2[kk] : f1[kk]));
+    // with one query tile the next group's operands are fetched now (unconditionally, so that
+    // the compiler counts the waits); with two there is no room for them and they are fetched
+    // after the group
     bf16x8 n1[KS], n2[KS];
-    fetch(grp + 1 < groups ? grp + 1 : grp, n1, n2);  // unconditional: counted waits
+    if (NQT == 1) fetch(grp + 1 < groups ? grp + 1 : grp, n1, n2);
     const bool ragged = kw0 + 32 > s.nk;
     f32x16 dk[NB];
 #pragma unroll
@@ -1339,10 +1342,14 @@ fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
         for (int nb = 0; nb < NB; ++nb) dst[nb * 32] = static_cast<__bf16>(dk[nb][r] * s.scale);
       }
     }
+    if (NQT == 1) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      f1[kk] = n1[kk];
-      f2[kk] = n2[kk];
+      for (int kk = 0; kk < KS; ++kk) {
+        f1[kk] = n1[kk];
+        f2[kk] = n2[kk];
+      }
+    } else if (grp + 1 < groups) {
+      fetch(grp + 1, f1, f2);
     }
   }
   // the block's partial dQ: the waves' accumulators summed in LDS, then written times scale

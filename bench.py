@@ -317,6 +317,52 @@ def fp8_mode(args):
     print(json.dumps(line), flush=True)
 
 
+def extra_hbm_mode(args):
+    """Device memory beyond inputs and outputs while the forward and the backward (setting 1)
+    run, at causal N = 16K, 32K, 64K (32 heads, d = 128): the driver's free bytes
+    (torch.cuda.mem_get_info, i.e. hipMemGetInfo) before and after, and the allocator's peak
+    above the resident tensors. The library allocates nothing and the one-pass paths take no
+    workspace, so both must be 0 at every N, against the N^2 bytes that P1 and P2 in bf16 would
+    take. Inputs are synthetic N(0, 1) (values do not matter for memory)."""
+    import torch
+    import online_attention_kl_amd as skl
+
+    dev = torch.device("cuda:0")
+    H, d = 32, 128
+    # load every kernel the measured calls use before the first reading
+    t = torch.randn(1, H, 256, d, device=dev).bfloat16()
+    kl, l1, l2 = skl.streamkl_fwd(t, t, t, t, causal=True)
+    g0 = torch.ones(1, H, 256, device=dev)
+    skl.streamkl_bwd_fixP1(t, t, t, t, l1, l2, g0, causal=True)
+    torch.cuda.synchronize()
+    del t, kl, l1, l2, g0
+    rows = []
+    for n in (16384, 32768, 65536):
+        q1, k1, q2, k2 = (torch.randn(1, H, n, d, device=dev).bfloat16() for _ in range(4))
+        g = torch.ones(1, H, n, device=dev)
+        out = tuple(torch.empty(1, H, n, device=dev) for _ in range(3))
+        grads = (torch.empty_like(q2), torch.empty_like(k2))
+        torch.cuda.synchronize()
+        resident = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        free0, total = torch.cuda.mem_get_info(dev)
+        skl.streamkl_fwd(q1, k1, q2, k2, causal=True, out=out)
+        skl.streamkl_bwd_fixP1(q1, k1, q2, k2, out[1], out[2], g, causal=True, out=grads)
+        torch.cuda.synchronize()
+        free1, _ = torch.cuda.mem_get_info(dev)
+        rows.append({"n": n, "inputs_bytes": 4 * q1.numel() * 2, "saved_state_bytes": 3 * n * H * 4,
+                     "gradient_bytes": 2 * q1.numel() * 2,
+                     "driver_free_bytes_change": int(free0 - free1),
+                     "allocator_peak_above_resident": int(torch.cuda.max_memory_allocated(dev) -
+                                                          resident),
+                     "p1_p2_bf16_bytes_avoided": 2 * H * n * n * 2})
+        del q1, k1, q2, k2, g, out, grads
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "extra_hbm", "unit": "bytes", "data": "synthetic",
+                      "config": {"heads": H, "head_dim": d, "causal": True,
+                                 "backward_settings": [1]}, "rows": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,6 +379,9 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="time the fp8 e4m3 forward against the bf16 forward on --workload and "
                          "report the effect of the fp8 input rounding on KL and LSE")
+    ap.add_argument("--extra-hbm", action="store_true",
+                    help="device memory beyond inputs and outputs during forward + backward at "
+                         "causal N = 16K, 32K, 64K (one JSON line)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter runs into profiles/hbm_traffic.json "
                          "(no GPU work)")
@@ -351,6 +400,9 @@ def main():
         return
     if args.fp8:
         fp8_mode(args)
+        return
+    if args.extra_hbm:
+        extra_hbm_mode(args)
         return
     w = WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)

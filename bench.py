@@ -317,6 +317,49 @@ def fp8_mode(args):
     print(json.dumps(line), flush=True)
 
 
+class ClockSampler:
+    """Samples the GPU's shader clock (amdsmi, clock type SYS) every `period` seconds in a
+    background thread while the timed steps run, so that throttling below the 2.4 GHz the peak
+    is quoted at is visible in the bench line. Reports None when amdsmi is unavailable."""
+
+    def __init__(self, period=0.02):
+        import threading
+        self.period, self.samples, self.error = period, [], None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            try:
+                h = amdsmi.amdsmi_get_processor_handles()[0]
+                while not self._stop.is_set():
+                    clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)["clk"]
+                    if isinstance(clk, (int, float)):
+                        self.samples.append(float(clk))
+                    self._stop.wait(self.period)
+            finally:
+                amdsmi.amdsmi_shut_down()
+        except Exception as e:  # no amdsmi, no permission: report nothing
+            self.error = f"{type(e).__name__}: {e}"
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=5)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v),
+                "source": "amdsmi SYS clock during the timed steps"}
+
+
 def extra_hbm_mode(args):
     """Device memory beyond inputs and outputs while the forward and the backward (setting 1)
     run, at causal N = 16K, 32K, 64K (32 heads, d = 128): the driver's free bytes
@@ -464,11 +507,12 @@ def main():
            for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            step(evs[k])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     kms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
     peak_extra = torch.cuda.max_memory_allocated(dev) - base_bytes
@@ -511,6 +555,7 @@ def main():
             "saved_state_bytes": 3 * B * H * nq * 4,
             "peak_extra_hbm_bytes_during_step": int(peak_extra),
             "materialised_p1_p2_bf16_bytes_avoided": 2 * B * H * nq * nk * 2,
+            "sclk_mhz": clocks.summary(),
         },
         "roofline": {
             "bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),

@@ -107,6 +107,52 @@ def write_traffic(fetch_dir: str, write_dir: str, workload: str) -> dict:
     return out
 
 
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU. GRBM_GUI_ACTIVE is read once per XCD, so a
+# dispatch's GPU cycles are its sum over the XCDs divided by 8.
+N_XCD, N_SIMD = 8, 256 * 4
+
+
+def summarize_counters(dirs) -> str:
+    """Markdown table of per-dispatch averages of rocprofv3 counter runs (`--pmc`, csv) over the
+    StreamKL kernels, with the derived MFMA utilisation: SQ_VALU_MFMA_BUSY_CYCLES (summed over
+    all SIMDs) over the dispatch's cycles times the SIMD count."""
+    import csv
+    import glob
+    import re
+
+    tot, disp = {}, {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for r in csv.DictReader(open(files[0])):
+            m = re.search(r"(fwd|dq|dk)_kernel", r["Kernel_Name"])
+            if not m:
+                continue
+            k = m.group(0)
+            c = tot.setdefault(k, {}).setdefault(r["Counter_Name"], [0.0, set()])
+            c[0] += float(r["Counter_Value"])
+            c[1].add((d, r["Dispatch_Id"]))
+
+    def avg(k, name):
+        c = tot[k].get(name)
+        return c[0] / len(c[1]) if c else None
+
+    cols = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_MFMA",
+            "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS"]
+    lines = ["| kernel | GPU cycles | MFMA busy | MFMA+VALU co-issue (of busy) | "
+             + " | ".join(cols[2:]) + " |", "|---" * (4 + len(cols) - 2) + "|"]
+    for k in sorted(tot):
+        cyc = avg(k, "GRBM_GUI_ACTIVE")
+        busy, co = avg(k, cols[0]), avg(k, cols[1])
+        cyc_s = f"{cyc / N_XCD:.4g}" if cyc else "n/a"
+        busy_s = f"{100 * busy / (cyc / N_XCD * N_SIMD):.1f} %" if busy and cyc else "n/a"
+        co_s = f"{100 * co / busy:.1f} %" if co and busy else "n/a"
+        rest = [f"{avg(k, c):.4g}" if avg(k, c) is not None else "n/a" for c in cols[2:]]
+        lines.append(f"| {k} | {cyc_s} | {busy_s} | {co_s} | " + " | ".join(rest) + " |")
+    return "\n".join(lines)
+
+
 def cpu_baseline(w, x, target_s: float):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload: blocks of 256
     query rows spread evenly over the row range of several slices, forward plus the workload's
@@ -428,9 +474,15 @@ def main():
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter runs into profiles/hbm_traffic.json "
                          "(no GPU work)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="markdown table of rocprofv3 --pmc runs over the StreamKL kernels, with "
+                         "the MFMA utilisation (no GPU work)")
     args = ap.parse_args()
     if args.write_traffic:
         print(json.dumps(write_traffic(*args.write_traffic, args.workload), indent=1))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the StreamKL path here runs on a single MI355X "

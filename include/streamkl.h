@@ -14,7 +14,8 @@
  *  - Tensors q1, q2 are [batch, heads, n_q, head_dim] and k1, k2 are [batch, heads, n_k,
  *    head_dim], bfloat16, in device memory, addressed through the element strides of
  *    streamkl_problem_t (the head_dim axis is contiguous). All pointers must be 16-byte aligned
- *    and every stride a multiple of 8 elements.
+ *    and every stride a multiple of 8 elements. Row strides of 16 MiB or more are not supported
+ *    (STREAMKL_ERROR_NOT_SUPPORTED): tiles are addressed with 32-bit offsets from a tile base.
  *  - Causal masking is top-left: key j is visible to query i iff j <= i. Every row then has at
  *    least one visible key.
  *  - Logits are S_t = scale * Q_t K_t^T; LSE values use the natural logarithm.
@@ -43,7 +44,7 @@ extern "C" {
 typedef enum {
   STREAMKL_SUCCESS = 0,
   STREAMKL_ERROR_INVALID_VALUE = 1, /* bad pointer, size, stride, alignment or overlap */
-  STREAMKL_ERROR_NOT_SUPPORTED = 2, /* valid but unsupported (head_dim not 64 or 128) */
+  STREAMKL_ERROR_NOT_SUPPORTED = 2, /* valid but unsupported (head_dim, row stride, n_q) */
   STREAMKL_ERROR_HIP = 3            /* the HIP runtime reported an error (no device, launch) */
 } streamkl_status_t;
 
@@ -53,8 +54,8 @@ typedef struct {
   int64_t n_q;          /* query rows per slice, >= 1 */
   int64_t n_k;          /* key rows per slice, >= 1 */
   int64_t head_dim;     /* 64 or 128 */
-  int64_t q_stride[3];  /* element strides of (batch, head, row) for q1 and q2 */
-  int64_t k_stride[3];  /* element strides of (batch, head, row) for k1 and k2 */
+  int64_t q_stride[3];  /* element strides of (batch, head, row) for q1 and q2; row < 16 MiB */
+  int64_t k_stride[3];  /* element strides of (batch, head, row) for k1 and k2; row < 16 MiB */
   float scale;          /* logit scale, finite and > 0 (1/sqrt(head_dim) is usual) */
   int32_t causal;       /* 0: every key visible; 1: top-left causal mask */
 } streamkl_problem_t;

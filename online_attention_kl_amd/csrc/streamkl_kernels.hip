@@ -122,6 +122,34 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
 template <int D>
 constexpr int lds_pitch() { return D + 8; }
 
+// Streamed tiles are read through buffer resources (a scalar base address and a byte range):
+// a load is the scalar base plus the thread's 32-bit offset plus a scalar offset, with no
+// 64-bit address arithmetic per load, and the hardware's range check returns 0 for every byte
+// past the range, which pads the ragged end of a matrix with zero rows without a per-row test.
+// Row strides are kept below kMaxRowStrideBytes so that the offsets within a staged block of
+// up to 128 rows fit in 32 bits (the C ABI rejects larger ones).
+constexpr long long kMaxRowStrideBytes = 1LL << 24;
+constexpr int kBufferWord3 = 0x00020000;  // 32-bit data format, no swizzle, raw addressing
+
+// Resource for `rows` rows (clamped to [0, MAXR], MAXR <= 128) of rstride bytes from p.
+template <int MAXR>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int rows,
+                                                            long long rstride) {
+  static_assert(MAXR <= 128, "MAXR rows of a stride below kMaxRowStrideBytes fit in 31 bits");
+  const int n = rows < 0 ? 0 : (rows > MAXR ? MAXR : rows);
+  // uniform by construction; readfirstlane keeps the range in a scalar register (a resource in
+  // vector registers would make every load a loop over the lanes' distinct values)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                           __builtin_amdgcn_readfirstlane(n * (int)rstride),
+                                           kBufferWord3);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                               unsigned soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Registers that stage ROWS rows of ROWB bytes from global memory into an LDS tile with a
 // pitch of ROWB + 16 bytes (the forward's key tiles, any element format).
 template <int ROWS, int ROWB, int NT>
@@ -129,24 +157,20 @@ struct TileRegs {
   static constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
   static constexpr int N = (ROWS * CPR + NT - 1) / NT;
   static constexpr bool EVEN = N * NT == ROWS * CPR;  // else threads past the tile idle
+  static_assert(NT % CPR == 0 && ROWS <= 128, "thread t: chunk t % CPR of rows t / CPR + k NT / CPR");
   uint4 v[N];
 
-  // Rows row0.. of a [n_valid, ROWB bytes] matrix with a row stride of rstride bytes; rows
-  // >= n_valid read as 0.
+  // Rows row0.. of a [n_valid, ROWB bytes] matrix with a row stride of rstride bytes
+  // (< kMaxRowStrideBytes); rows >= n_valid read as 0.
   __device__ __forceinline__ void load(const uint8_t* __restrict__ base, long long rstride,
                                        int row0, int n_valid) {
-    const bool full = row0 + ROWS <= n_valid;  // block-uniform: no per-row checks needed
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc<ROWS>(base + (long long)row0 * rstride, n_valid - row0, rstride);
+    const unsigned off = (threadIdx.x / CPR) * (unsigned)rstride + (threadIdx.x % CPR) * 16u;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = threadIdx.x + i * NT;
-      const int row = idx / CPR, c = idx % CPR;
-      const int gr = row0 + row;
-      const uint8_t* src = base + (long long)gr * rstride + c * 16;
-      if ((EVEN || idx < ROWS * CPR) && (full || gr < n_valid))
-        v[i] = *reinterpret_cast<const uint4*>(src);
-      else
-        v[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int i = 0; i < N; ++i)
+      if (EVEN || threadIdx.x + i * NT < ROWS * CPR)
+        v[i] = buffer_load16(r, off, (unsigned)(i * (NT / CPR)) * (unsigned)rstride);
   }
   __device__ __forceinline__ void store(uint8_t* lds) const {
 #pragma unroll
@@ -680,18 +704,26 @@ struct BwdStage {
     chunk = rem / kBT;
     return gid < NTENS * PER;
   }
+  // Rows row0.. of two [n_valid, D] matrices with a row stride of rstride elements
+  // (< kMaxRowStrideBytes / 2); rows >= n_valid read as 0.
   __device__ __forceinline__ void load(const uint16_t* __restrict__ b0,
                                        const uint16_t* __restrict__ b1, long long rstride,
                                        int row0, int n_valid) {
-    const bool full = row0 + kBT <= n_valid;  // block-uniform: no per-row checks needed
+    static_assert(PER % 64 == 0, "a wave's chunks belong to one tensor");
+    const __amdgpu_buffer_rsrc_t r0 =
+        make_rsrc<kBT>(b0 + (long long)row0 * rstride, n_valid - row0, rstride * 2);
+    const __amdgpu_buffer_rsrc_t r1 =
+        make_rsrc<kBT>(b1 + (long long)row0 * rstride, n_valid - row0, rstride * 2);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       int te, row, chunk;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (mine(i, te, row, chunk) && (full || row0 + row < n_valid))
-        val = *reinterpret_cast<const uint4*>((te == 0 ? b0 : b1) +
-                                              (long long)(row0 + row) * rstride + chunk * 8);
-      v[i] = val;
+      if (!mine(i, te, row, chunk)) {
+        v[i] = make_uint4(0u, 0u, 0u, 0u);  // never stored
+        continue;
+      }
+      // the tensor index is the same for the whole wave: choose the resource as a scalar
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_readfirstlane(te) == 0 ? r0 : r1;
+      v[i] = buffer_load16(r, (unsigned)row * (unsigned)(rstride * 2) + (unsigned)chunk * 16u, 0u);
     }
   }
   // Row-major copies of every tensor; transposed copy of tensor `free_te`.
@@ -1422,6 +1454,9 @@ streamkl_status_t validate(const streamkl_problem_t* p, const void* q1, const vo
   }
   if (p->q_stride[2] < p->head_dim || p->k_stride[2] < p->head_dim)
     return fail(STREAMKL_ERROR_INVALID_VALUE, "row stride must be >= head_dim");
+  if (p->q_stride[2] * elem_bytes >= kMaxRowStrideBytes ||
+      p->k_stride[2] * elem_bytes >= kMaxRowStrideBytes)
+    return fail(STREAMKL_ERROR_NOT_SUPPORTED, "row strides must be below 16 MiB");
   const void* in[4] = {q1, k1, q2, k2};
   for (const void* x : in) {
     if (!x) return fail(STREAMKL_ERROR_INVALID_VALUE, "input pointer is NULL");

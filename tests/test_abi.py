@@ -86,6 +86,16 @@ def test_invalid_problem_values():
     p = good_problem()
     p.k_stride[2] = 64
     assert fwd(p) == 1
+    # row strides of 16 MiB or more are not supported (32-bit offsets within a staged tile)
+    p = good_problem()
+    p.k_stride[2] = 1 << 23
+    p.k_stride[1] = 80 << 23
+    p.k_stride[0] = 160 << 23
+    assert fwd(p) == 2 and "16 MiB" in last_error()
+    p.k_stride[2] = (1 << 23) - 8
+    # accepted by the stride check; the (fake) outputs then fall inside the 2.6 GB key span,
+    # so the call still stops in validation, before any launch
+    assert fwd(p) == 1 and "overlap" in last_error()
 
 
 def test_invalid_pointers():

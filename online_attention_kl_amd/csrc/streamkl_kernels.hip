@@ -136,7 +136,11 @@ template <int MAXR>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int rows,
                                                             long long rstride) {
   static_assert(MAXR <= 128, "MAXR rows of a stride below kMaxRowStrideBytes fit in 31 bits");
-  const int n = rows < 0 ? 0 : (rows > MAXR ? MAXR : rows);
+  int m = rows < MAXR ? rows : MAXR;
+  // pinned to a scalar register between the two clamps: otherwise the pair is fused into a
+  // vector median instruction, and the result has to be moved back to a scalar register
+  asm volatile("" : "+s"(m));
+  const int n = m > 0 ? m : 0;
   // uniform by construction; readfirstlane keeps the range in a scalar register (a resource in
   // vector registers would make every load a loop over the lanes' distinct values)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
@@ -702,7 +706,7 @@ struct BwdStage {
     const int rem = gid - te * PER;
     row = rem % kBT;
     chunk = rem / kBT;
-    return gid < NTENS * PER;
+    return NTENS * PER % kBwdThreads == 0 || gid < NTENS * PER;  // every thread has N chunks
   }
   // Rows row0.. of two [n_valid, D] matrices with a row stride of rstride elements
   // (< kMaxRowStrideBytes / 2); rows >= n_valid read as 0.

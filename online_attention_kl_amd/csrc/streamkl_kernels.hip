@@ -28,7 +28,9 @@
 //    and never use atomics: results are deterministic.
 //  * Streamed tiles sit in double-buffered LDS with rows padded by 16 bytes, so the 16 rows read
 //    by one 16-byte operand load fall in distinct banks and every operand address is a base
-//    register plus an immediate.
+//    register plus an immediate. They are loaded from HBM through buffer resources (scalar base
+//    and byte range per stage, 32-bit per-thread offsets); the range check pads the ragged end
+//    with zero rows.
 //  * exp and log use the hardware base-2 instructions; scale * log2(e) is folded into one FMA
 //    per element and the saved LSEs stay in natural-log units.
 //  * Causal (top-left) masking skips whole tiles past the frontier; only tiles that straddle

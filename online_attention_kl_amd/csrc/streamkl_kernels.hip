@@ -150,6 +150,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int r
                                            kBufferWord3);
 }
 
+// voff is range-checked against the resource; soff is added to the address unchecked.
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned voff,
                                                unsigned soff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
@@ -173,10 +174,12 @@ struct TileRegs {
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc<ROWS>(base + (long long)row0 * rstride, n_valid - row0, rstride);
     const unsigned off = (threadIdx.x / CPR) * (unsigned)rstride + (threadIdx.x % CPR) * 16u;
+    // the whole offset goes into the vector operand: the range check covers the vector and
+    // instruction offsets but not the scalar one
 #pragma unroll
     for (int i = 0; i < N; ++i)
       if (EVEN || threadIdx.x + i * NT < ROWS * CPR)
-        v[i] = buffer_load16(r, off, (unsigned)(i * (NT / CPR)) * (unsigned)rstride);
+        v[i] = buffer_load16(r, off + (unsigned)(i * (NT / CPR)) * (unsigned)rstride, 0u);
   }
   __device__ __forceinline__ void store(uint8_t* lds) const {
 #pragma unroll

@@ -210,9 +210,11 @@ def small_nq(args):
     """Few query rows (decode-like), 32 heads, 64K keys, d=128, non-causal, backward setting 1:
     one JSON line per N_Q with the one-pass forward against the split-K forward and the
     one-kernel dQ against the key-split dQ (dK alongside), and for N_Q <= 64 the fused backward
-    (one key-major pass for dQ and dK). The split-K forward reads every key once, so its
-    roofline is HBM bandwidth: algorithmic bytes = Q1, Q2, K1, K2 read once plus KL, LSE1, LSE2
-    written, over the duration of the call (split kernel + merge kernel)."""
+    (one key-major pass for dQ and dK). Up to 64 rows the split-K forward's wavefront work items
+    read every key once, so its roofline is HBM bandwidth: algorithmic bytes = Q1, Q2, K1, K2
+    read once plus KL, LSE1, LSE2 written, over the duration of the call (split kernel + merge
+    kernel). Above 64 rows the key ranges run on the LDS-staged forward kernel and the roofline
+    is the bf16 MFMA one (4 d flop per pair)."""
     import numpy as np
     import torch
     import online_attention_kl_amd as skl
@@ -273,6 +275,18 @@ def small_nq(args):
             ms[name] = e0.elapsed_time(e1) / args.steps
         fbytes = B * H * (2 * nq * d * 2 + 2 * nk * d * 2 + 3 * nq * 4)
         gbs = fbytes / (ms["fwd_split_k"] * 1e-3) / 1e9
+        if nq <= 64:
+            # wavefront work items read every key once: HBM-bound
+            roof = {"kernel": "fwd_split_kernel + fwd_merge_kernel", "bound": "hbm",
+                    "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                    "frac": round(gbs / 8000.0, 4), "traffic": None}
+        else:
+            # key ranges on the LDS-staged kernel: 4 d flop per pair on the bf16 MFMA
+            tfs = 4 * d * B * H * nq * nk / (ms["fwd_split_k"] * 1e-3) / 1e12
+            roof = {"kernel": "fwd_kernel (key ranges) + fwd_merge_kernel", "bound": "mfma",
+                    "achieved": round(tfs, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tfs / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "hbm_gbs": round(gbs, 1)}
         line = {
             "mode": "small_nq", "unit": "ms", "steps": args.steps, "warmup": args.warmup,
             "data": "synthetic",
@@ -289,9 +303,7 @@ def small_nq(args):
                         "backward_fused_vs_one_kernel": (
                             round((ms["dq_one_kernel"] + ms["dk"]) / ms["bwd_fused"], 2)
                             if fused else None)},
-            "roofline": {"kernel": "fwd_split_kernel + fwd_merge_kernel", "bound": "hbm",
-                         "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                         "frac": round(gbs / 8000.0, 4), "traffic": None},
+            "roofline": roof,
         }
         print(json.dumps(line), flush=True)
 

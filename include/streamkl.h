@@ -103,17 +103,20 @@ streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* problem, float desc
  * de Kernel de GPU", Split-K variant; its gain for small N_Q under "Resultados Experimentais",
  * ablation). Same outputs and semantics as streamkl_fwd, for any sizes.
  *
- * The keys of every slice are cut into n_splits contiguous ranges of whole 32-key tiles. Each
- * (slice, 32-row query block, range) is one independent work item of one wavefront, which
- * writes the partial online state (m1, l1, m2, l2, acc) of its rows to the workspace; a second
- * kernel merges the ranges of each row (the online state of a union of key sets follows from
- * the states of its parts: the larger maximum wins and the other sums are rescaled) and writes
- * kl, lse1, lse2. Results agree with streamkl_fwd to float32 rounding (summation order differs)
- * and are bitwise deterministic for a given n_splits.
+ * The keys of every slice are cut into n_splits contiguous ranges of whole key granules. With
+ * n_q <= 64 a granule is a 32-key tile and each (slice, 32-row query block, range) is one
+ * independent work item of one wavefront that reads its keys straight from memory; with
+ * n_q > 64 a granule is a 64-key stage and each (slice, 256-row query block, range) is one
+ * block of the LDS-staged forward kernel, so that the query rows of a block share every key
+ * read. Either way the work item writes the partial online state (m1, l1, m2, l2, acc) of its
+ * rows to the workspace; a second kernel merges the ranges of each row (the online state of a
+ * union of key sets follows from the states of its parts: the larger maximum wins and the other
+ * sums are rescaled) and writes kl, lse1, lse2. Results agree with streamkl_fwd to float32
+ * rounding (summation order differs) and are bitwise deterministic for a given n_splits.
  *
  * n_splits: requested number of ranges; <= 0 chooses streamkl_fwd_splitk_default_splits().
- *   The number used is min(n_splits, number of key tiles, 4096), then reduced so that no range
- *   is empty.
+ *   The number used is min(n_splits, number of key granules, 4096), then reduced so that no
+ *   range is empty.
  * workspace: device memory of at least streamkl_fwd_splitk_workspace_size(problem, n_splits)
  *   bytes, 16-byte aligned, owned by the caller, not overlapping any input or output; its
  *   contents on entry are ignored and on return are unspecified. It holds float32
@@ -121,10 +124,10 @@ streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* problem, float desc
  * Errors: as streamkl_fwd, plus STREAMKL_ERROR_INVALID_VALUE for a NULL, misaligned,
  *   overlapping or too small workspace.
  */
-/* Number of key ranges chosen for n_splits <= 0: about 4096 work items with at least 8 key
- * tiles per range (only tiles some row can see count when causal); 1 when there are more than
- * 256 work items without splitting, where streamkl_fwd is the faster path. 0 for a NULL problem
- * or sizes < 1. */
+/* Number of key ranges chosen for n_splits <= 0: about 4096 wavefront work items (n_q <= 64)
+ * or 512 block work items (n_q > 64), with at least 8 key granules per range (only keys some
+ * row can see count when causal); 1 when there are more than 256 work items without splitting,
+ * where streamkl_fwd is the faster path. 0 for a NULL problem or sizes < 1. */
 int32_t streamkl_fwd_splitk_default_splits(const streamkl_problem_t* problem);
 /* Workspace bytes streamkl_fwd_splitk needs for this n_splits; 0 for a NULL problem or sizes
  * < 1. */

@@ -338,22 +338,35 @@ constexpr int kFwdThreads = 64 * kFwdWaves;
 
 // F: input format (Bf16In or Fp8In). q*/k* point at elements of that format; strides in the
 // Shape are in elements. Side t's logits are scale * sigma_t * Q_t K_t^T.
-template <class F, int D, bool CAUSAL, bool SHARED_K>
+// SPLIT (bf16 only): every block covers one key range of split_keys keys (a multiple of the
+// stage) as well as one query block, and writes the partial state of its rows (M1, l1, M2, l2,
+// acc, as the split-K kernel below does) to part [slice][range][5][n_q] instead of the outputs;
+// fwd_merge_kernel finishes them.
+template <class F, int D, bool CAUSAL, bool SHARED_K, bool SPLIT = false>
 __global__ void __launch_bounds__(kFwdThreads, kFwdBlocksPerCU)
 fwd_kernel(const uint8_t* __restrict__ q1, const uint8_t* __restrict__ k1,
            const uint8_t* __restrict__ q2, const uint8_t* __restrict__ k2,
            float* __restrict__ kl_out, float* __restrict__ lse1_out,
-           float* __restrict__ lse2_out, Shape s, float sigma1, float sigma2) {
+           float* __restrict__ lse2_out, Shape s, float sigma1, float sigma2,
+           float* __restrict__ part = nullptr, int nsplit = 1, int split_keys = 0) {
   constexpr int EB = F::EB, KPER = F::KPER, KS = D / KPER;
   constexpr int RB = kFwdRB, BK = 32 * RB, SB = kFwdSB, BQ = 32 * kFwdWaves;
   constexpr int NKT = SHARED_K ? 1 : 2;
   static_assert(SB % BK == 0, "a stage holds whole tiles");
+  static_assert(!SPLIT || std::is_same<F, Bf16In>::value, "key ranges: bf16 inputs");
   constexpr int ROWB = D * EB, PB = ROWB + 16, TILE = SB * PB;  // bytes
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NKT * TILE];
 
+  // block id = (range * query blocks + rank) * slices + slice: every block of a slice, whatever
+  // its range, lands on the same XCD
   int rank, slice;
   block_coords(s.bh, rank, slice);
   const int nqb = (s.nq + BQ - 1) / BQ;
+  int split = 0;
+  if (SPLIT) {
+    split = rank / nqb;
+    rank -= split * nqb;
+  }
   const int qb = CAUSAL ? nqb - 1 - rank : rank;
   const int b = slice / s.heads, hd = slice - b * s.heads;
   const uint8_t* Q1 = q1 + (b * s.q_sb + hd * s.q_sh) * EB;
@@ -377,9 +390,16 @@ fwd_kernel(const uint8_t* __restrict__ q1, const uint8_t* __restrict__ k1,
   }
 
   const int last_q = min(s.nq - 1, qb * BQ + BQ - 1);
-  const int kend = CAUSAL ? min(s.nk, last_q + 1) : s.nk;
-  const int ntiles = (kend + BK - 1) / BK;
-  const int nstages = (kend + SB - 1) / SB;
+  const int kvis = CAUSAL ? min(s.nk, last_q + 1) : s.nk;
+  // keys [kbeg, kend) of this block; tile t starts at key kbeg + t BK
+  const int kbeg = SPLIT ? split * split_keys : 0;
+  const int kend = SPLIT ? min(kvis, kbeg + split_keys) : kvis;
+  const int nkeys = kend > kbeg ? kend - kbeg : 0;
+  const int ntiles = (nkeys + BK - 1) / BK;
+  const int nstages = (nkeys + SB - 1) / SB;
+  const uint8_t* K1r = K1 + (long long)kbeg * krs;
+  const uint8_t* K2r = K2 + (long long)kbeg * krs;
+  const int nk_r = s.nk - kbeg;  // rows of the key matrices from kbeg on
   const float c1 = s.scale * sigma1 * kLog2e, c2 = s.scale * sigma2 * kLog2e;
   const float r12 = sigma1 / sigma2;
   const bool wave_live = qw0 < s.nq;
@@ -388,13 +408,13 @@ fwd_kernel(const uint8_t* __restrict__ q1, const uint8_t* __restrict__ k1,
   float m1 = kNegBig, m2 = kNegBig, nb1 = 0.f, nb2 = 0.f;
   float L1[NP] = {}, L2[NP] = {}, A[NP] = {};
   TileRegs<SB, ROWB, kFwdThreads> r1, r2;
-  r1.load(K1, krs, 0, s.nk);
-  if (!SHARED_K) r2.load(K2, krs, 0, s.nk);
+  r1.load(K1r, krs, 0, nk_r);
+  if (!SHARED_K) r2.load(K2r, krs, 0, nk_r);
   r1.store(lds);
   if (!SHARED_K) r2.store(lds + TILE);
   if (nstages > 1) {
-    r1.load(K1, krs, SB, s.nk);
-    if (!SHARED_K) r2.load(K2, krs, SB, s.nk);
+    r1.load(K1r, krs, SB, nk_r);
+    if (!SHARED_K) r2.load(K2r, krs, SB, nk_r);
   }
   __syncthreads();
 
@@ -429,7 +449,7 @@ fwd_kernel(const uint8_t* __restrict__ q1, const uint8_t* __restrict__ k1,
 #pragma unroll
     for (int sub = 0; sub < SB / BK; ++sub) {
       const int t = st * (SB / BK) + sub;
-      const int key0 = t * BK;
+      const int key0 = kbeg + t * BK;
       // a tile is skipped when it is past the end or every key of it is past this wave's rows
       if (t < ntiles && wave_live && !(CAUSAL && key0 > qw0 + 31)) {
         contract(kt1, kt2, sub * BK);
@@ -450,8 +470,8 @@ fwd_kernel(const uint8_t* __restrict__ q1, const uint8_t* __restrict__ k1,
       r1.store(nxt);
       if (!SHARED_K) r2.store(nxt + TILE);
       if (st + 2 < nstages) {
-        r1.load(K1, krs, (st + 2) * SB, s.nk);
-        if (!SHARED_K) r2.load(K2, krs, (st + 2) * SB, s.nk);
+        r1.load(K1r, krs, (st + 2) * SB, nk_r);
+        if (!SHARED_K) r2.load(K2r, krs, (st + 2) * SB, nk_r);
       }
     }
     __syncthreads();
@@ -469,7 +489,7 @@ fwd_kernel(const uint8_t* __restrict__ q1, const uint8_t* __restrict__ k1,
 #pragma unroll
     for (int j = 0; j < NP; ++j) L1[j] = L2[j] = A[j] = 0.f;
     const int wend = CAUSAL ? min(kend, qw0 + 32) : kend;
-    for (int key0 = 0; key0 < wend; key0 += 32) {
+    for (int key0 = kbeg; key0 < wend; key0 += 32) {
       f32x16 x1[1] = {f32x16{}}, x2[1] = {f32x16{}};
       const long long ro = (long long)min(key0 + col, s.nk - 1) * krs + lane_off;
 #pragma unroll
@@ -496,12 +516,21 @@ fwd_kernel(const uint8_t* __restrict__ q1, const uint8_t* __restrict__ k1,
     const float L1s = l1 * fa + ol1 * fb;
     const float L2s = l2 * ga + ol2 * gb;
     const float As = acc * fa + oacc * fb;
-    const float lse1 = M1 * (s.scale * sigma1) + log2_hw(L1s) * kLn2;
-    const float lse2 = M2 * (s.scale * sigma2) + log2_hw(L2s) * kLn2;
-    const long long o = (long long)slice * s.nq + query;
-    kl_out[o] = (s.scale * sigma2) * As / L1s + (lse2 - lse1);
-    lse1_out[o] = lse1;
-    lse2_out[o] = lse2;
+    if constexpr (SPLIT) {
+      float* o = part + ((long long)slice * nsplit + split) * 5 * s.nq + query;
+      o[0] = M1;
+      o[s.nq] = L1s;
+      o[2 * s.nq] = M2;
+      o[3 * s.nq] = L2s;
+      o[4 * s.nq] = As;
+    } else {
+      const float lse1 = M1 * (s.scale * sigma1) + log2_hw(L1s) * kLn2;
+      const float lse2 = M2 * (s.scale * sigma2) + log2_hw(L2s) * kLn2;
+      const long long o = (long long)slice * s.nq + query;
+      kl_out[o] = (s.scale * sigma2) * As / L1s + (lse2 - lse1);
+      lse1_out[o] = lse1;
+      lse2_out[o] = lse2;
+    }
   }
 }
 
@@ -1535,50 +1564,76 @@ void dispatch_fwd(int64_t d, bool causal, bool sk, const Shape& s, const void* q
 #undef SKL_FWD
 }
 
-// Key ranges of the split-K forward: n_splits requested (<= 0: chosen here) -> tiles per range
-// and the number of ranges actually used (no range is empty of tiles).
+// Key ranges of the split-K forward: n_splits requested (<= 0: chosen here) -> keys per range
+// and the number of ranges actually used (no range is empty of key granules). Up to two 32-row
+// query blocks per slice (n_q <= 64) every wave is a work item that reads its keys straight
+// from global memory (granules of 32 keys); with more query rows those waves would each read
+// the same keys again, so the work items are blocks of the LDS-staged forward kernel, one
+// 256-row query block by one key range (granules of one 64-key stage).
+constexpr int kSplitWaveMaxRows = 64;
+
 struct SplitPlan {
   int nsplit, split_keys;
+  bool blocks;  // ranges run on the LDS-staged forward kernel
 };
 
 SplitPlan split_plan(const streamkl_problem_t* p, int32_t n_splits) {
+  const bool blocks = p->n_q > kSplitWaveMaxRows;
+  const int64_t gran = blocks ? kFwdSB : 32;
   // with the top-left causal mask no row sees a key past n_q - 1
   const int64_t nvis = p->causal && p->n_q < p->n_k ? p->n_q : p->n_k;
-  const int64_t ntiles = (nvis + 31) / 32;
-  const int64_t items = p->batch * p->heads * ((p->n_q + 31) / 32);
+  const int64_t ngran = (nvis + gran - 1) / gran;
+  const int64_t rows_per_item = blocks ? 32 * kFwdWaves : 32;
+  const int64_t items = p->batch * p->heads * ((p->n_q + rows_per_item - 1) / rows_per_item);
   int64_t ns = n_splits;
   if (ns <= 0) {
+    // wave items: about 4096 waves in flight (16 per CU); block items: about two blocks per CU
+    // (one resident at a time). At least 8 granules per range; no split at all when there are
+    // as many items as CUs already (the one-pass forward is then the better path).
+    const int64_t target = blocks ? 512 : 4096;
     if (items > 256) {
-      ns = 1;  // one work item per CU or more already: the one-pass forward is the better path
+      ns = 1;
     } else {
-      // about 4096 waves in flight (16 per CU), at least 8 key tiles per range
-      ns = (4096 + items - 1) / items;
-      const int64_t cap = (ntiles + 7) / 8;
+      ns = (target + items - 1) / items;
+      const int64_t cap = (ngran + 7) / 8;
       if (ns > cap) ns = cap;
     }
   }
-  if (ns > ntiles) ns = ntiles;
+  if (ns > ngran) ns = ngran;
   if (ns > 4096) ns = 4096;
   if (ns < 1) ns = 1;
-  const int64_t tiles_per = (ntiles + ns - 1) / ns;
-  const int64_t used = (ntiles + tiles_per - 1) / tiles_per;
-  return {(int)used, (int)(tiles_per * 32)};
+  const int64_t per = (ngran + ns - 1) / ns;
+  const int64_t used = (ngran + per - 1) / per;
+  return {(int)used, (int)(per * gran), blocks};
 }
 
 size_t split_workspace_bytes(const streamkl_problem_t* p, int nsplit) {
   return (size_t)p->batch * p->heads * p->n_q * nsplit * 5 * sizeof(float);
 }
 
+// Blocks launched by the split-K forward for this plan.
+long long split_blocks(const Shape& s, const SplitPlan& plan) {
+  if (plan.blocks)
+    return (long long)s.bh * ((s.nq + 32 * kFwdWaves - 1) / (32 * kFwdWaves)) * plan.nsplit;
+  const long long items = (long long)s.bh * ((s.nq + 31) / 32) * plan.nsplit;
+  return (items + kSplitWaves - 1) / kSplitWaves;
+}
+
 template <int D, bool CAUSAL, bool SK>
 void launch_fwd_split(const Shape& s, const SplitPlan& plan, const void* q1, const void* k1,
                       const void* q2, const void* k2, float* part, float* kl, float* l1,
                       float* l2, hipStream_t st) {
-  const long long items = (long long)s.bh * ((s.nq + 31) / 32) * plan.nsplit;
-  const long long blocks = (items + kSplitWaves - 1) / kSplitWaves;
-  hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL, SK>), dim3((unsigned)blocks),
-                     dim3(64 * kSplitWaves), 0, st, (const uint16_t*)q1, (const uint16_t*)k1,
-                     (const uint16_t*)q2, (const uint16_t*)k2, part, s, plan.nsplit,
-                     plan.split_keys);
+  const long long blocks = split_blocks(s, plan);
+  if (plan.blocks)
+    hipLaunchKernelGGL((fwd_kernel<Bf16In, D, CAUSAL, SK, true>), dim3((unsigned)blocks),
+                       dim3(kFwdThreads), 0, st, (const uint8_t*)q1, (const uint8_t*)k1,
+                       (const uint8_t*)q2, (const uint8_t*)k2, nullptr, nullptr, nullptr, s, 1.f,
+                       1.f, part, plan.nsplit, plan.split_keys);
+  else
+    hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL, SK>), dim3((unsigned)blocks),
+                       dim3(64 * kSplitWaves), 0, st, (const uint16_t*)q1, (const uint16_t*)k1,
+                       (const uint16_t*)q2, (const uint16_t*)k2, part, s, plan.nsplit,
+                       plan.split_keys);
   const long long rows = (long long)s.bh * s.nq;
   int group = 1;  // lanes per row in the merge: the ranges' count rounded up to a power of two
   while (group < 64 && group < plan.nsplit) group *= 2;
@@ -1881,7 +1936,7 @@ streamkl_status_t streamkl_fwd_splitk(const streamkl_problem_t* p, const void* q
                          reinterpret_cast<uintptr_t>(workspace) + need}};
   st = check_outputs(p, q1, k1, q2, k2, outs, 4, "streamkl_fwd_splitk");
   if (st != STREAMKL_SUCCESS) return st;
-  if ((long long)s.bh * ((s.nq + 31) / 32) * plan.nsplit / kSplitWaves >= (1LL << 31))
+  if (split_blocks(s, plan) >= (1LL << 31))
     return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_fwd_splitk: grid too large");
   (void)hipGetLastError();
   const bool sk = k1 == k2, causal = p->causal != 0;

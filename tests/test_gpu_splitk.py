@@ -22,6 +22,11 @@ SHAPES = [
     (1, 2, 100, 257, 128, False),
     (1, 1, 70, 70, 64, True),
     (1, 32, 16, 65536, 128, False),
+    # more than 64 query rows: ranges run as blocks of the LDS-staged forward kernel
+    (1, 2, 300, 1000, 128, True),
+    (2, 2, 513, 777, 64, False),
+    (1, 3, 65, 2000, 128, False),
+    (1, 1, 700, 300, 64, True),
 ]
 
 

@@ -210,11 +210,10 @@ def small_nq(args):
     """Few query rows (decode-like), 32 heads, 64K keys, d=128, non-causal, backward setting 1:
     one JSON line per N_Q with the one-pass forward against the split-K forward and the
     one-kernel dQ against the key-split dQ (dK alongside), and for N_Q <= 64 the fused backward
-    (one key-major pass for dQ and dK). Up to 64 rows the split-K forward's wavefront work items
-    read every key once, so its roofline is HBM bandwidth: algorithmic bytes = Q1, Q2, K1, K2
-    read once plus KL, LSE1, LSE2 written, over the duration of the call (split kernel + merge
-    kernel). Above 64 rows the key ranges run on the LDS-staged forward kernel and the roofline
-    is the bf16 MFMA one (4 d flop per pair)."""
+    (one key-major pass for dQ and dK). The split-K forward's roofline is the HBM one
+    (algorithmic bytes = Q1, Q2, K1, K2 read once plus KL, LSE1, LSE2 written, over the duration
+    of the call: split kernel + merge kernel) while those bytes take longer at peak than the
+    4 d flop per pair on the bf16 MFMA, and the MFMA one above that."""
     import numpy as np
     import torch
     import online_attention_kl_amd as skl
@@ -275,18 +274,19 @@ def small_nq(args):
             ms[name] = e0.elapsed_time(e1) / args.steps
         fbytes = B * H * (2 * nq * d * 2 + 2 * nk * d * 2 + 3 * nq * 4)
         gbs = fbytes / (ms["fwd_split_k"] * 1e-3) / 1e9
-        if nq <= 64:
-            # wavefront work items read every key once: HBM-bound
-            roof = {"kernel": "fwd_split_kernel + fwd_merge_kernel", "bound": "hbm",
-                    "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                    "frac": round(gbs / 8000.0, 4), "traffic": None}
+        # the binding roofline is the one whose algorithmic time is longer: HBM for the bytes
+        # read once, bf16 MFMA for 4 d flop per pair (HBM up to N_Q ~ 300 at 64K keys)
+        flops = 4 * d * B * H * nq * nk
+        tfs = flops / (ms["fwd_split_k"] * 1e-3) / 1e12
+        kern = ("fwd_split_kernel" if nq <= 32 else "fwd_kernel (key ranges)") + \
+            " + fwd_merge_kernel"
+        if fbytes / 8.0e12 >= flops / (PEAK_BF16_TFLOPS * 1e12):
+            roof = {"kernel": kern, "bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0,
+                    "unit": "GB/s", "frac": round(gbs / 8000.0, 4), "traffic": None}
         else:
-            # key ranges on the LDS-staged kernel: 4 d flop per pair on the bf16 MFMA
-            tfs = 4 * d * B * H * nq * nk / (ms["fwd_split_k"] * 1e-3) / 1e12
-            roof = {"kernel": "fwd_kernel (key ranges) + fwd_merge_kernel", "bound": "mfma",
-                    "achieved": round(tfs, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tfs / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                    "hbm_gbs": round(gbs, 1)}
+            roof = {"kernel": kern, "bound": "mfma", "achieved": round(tfs, 1),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tfs / PEAK_BF16_TFLOPS, 4), "traffic": None}
         line = {
             "mode": "small_nq", "unit": "ms", "steps": args.steps, "warmup": args.warmup,
             "data": "synthetic",

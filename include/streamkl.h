@@ -104,9 +104,9 @@ streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* problem, float desc
  * ablation). Same outputs and semantics as streamkl_fwd, for any sizes.
  *
  * The keys of every slice are cut into n_splits contiguous ranges of whole key granules. With
- * n_q <= 64 a granule is a 32-key tile and each (slice, 32-row query block, range) is one
+ * n_q <= 32 a granule is a 32-key tile and each (slice, 32-row query block, range) is one
  * independent work item of one wavefront that reads its keys straight from memory; with
- * n_q > 64 a granule is a 64-key stage and each (slice, 256-row query block, range) is one
+ * n_q > 32 a granule is a 64-key stage and each (slice, 256-row query block, range) is one
  * block of the LDS-staged forward kernel, so that the query rows of a block share every key
  * read. Either way the work item writes the partial online state (m1, l1, m2, l2, acc) of its
  * rows to the workspace; a second kernel merges the ranges of each row (the online state of a
@@ -124,8 +124,8 @@ streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* problem, float desc
  * Errors: as streamkl_fwd, plus STREAMKL_ERROR_INVALID_VALUE for a NULL, misaligned,
  *   overlapping or too small workspace.
  */
-/* Number of key ranges chosen for n_splits <= 0: about 4096 wavefront work items (n_q <= 64)
- * or 512 block work items (n_q > 64), with at least 8 key granules per range (only keys some
+/* Number of key ranges chosen for n_splits <= 0: about 4096 wavefront work items (n_q <= 32)
+ * or 512 block work items (n_q > 32), with at least 8 key granules per range (only keys some
  * row can see count when causal); 1 when there are more than 256 work items without splitting,
  * where streamkl_fwd is the faster path. 0 for a NULL problem or sizes < 1. */
 int32_t streamkl_fwd_splitk_default_splits(const streamkl_problem_t* problem);

@@ -1565,12 +1565,14 @@ void dispatch_fwd(int64_t d, bool causal, bool sk, const Shape& s, const void* q
 }
 
 // Key ranges of the split-K forward: n_splits requested (<= 0: chosen here) -> keys per range
-// and the number of ranges actually used (no range is empty of key granules). Up to two 32-row
-// query blocks per slice (n_q <= 64) every wave is a work item that reads its keys straight
+// and the number of ranges actually used (no range is empty of key granules). With one 32-row
+// query block per slice (n_q <= 32) every wave is a work item that reads its keys straight
 // from global memory (granules of 32 keys); with more query rows those waves would each read
 // the same keys again, so the work items are blocks of the LDS-staged forward kernel, one
-// 256-row query block by one key range (granules of one 64-key stage).
-constexpr int kSplitWaveMaxRows = 64;
+// 256-row query block by one key range (granules of one 64-key stage). (32 heads, 64K keys:
+// the two paths take the same time at 24-32 rows; at 33-64 rows the blocks take 0.21 ms
+// against 0.25-0.29 ms.)
+constexpr int kSplitWaveMaxRows = 32;
 
 struct SplitPlan {
   int nsplit, split_keys;

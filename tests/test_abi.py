@@ -128,13 +128,13 @@ def test_splitk_plan_and_workspace_size():
     L = skl.lib()
     assert L.streamkl_fwd_splitk_default_splits(None) == 0
     assert L.streamkl_fwd_splitk_workspace_size(None, 4) == 0
-    for nq, nk in ((1, 65536), (16, 4096), (64, 80), (300, 33), (7, 1), (65, 4096),
+    for nq, nk in ((1, 65536), (16, 4096), (64, 80), (300, 33), (7, 1), (33, 4096), (65, 4096),
                    (512, 65536), (2000, 1000)):
         p = good_problem()
         p.n_q, p.n_k = nq, nk
-        # key granules of a range: 32 keys for wave work items (n_q <= 64), else one 64-key
+        # key granules of a range: 32 keys for wave work items (n_q <= 32), else one 64-key
         # stage of the LDS-staged kernel
-        ntiles = (nk + 31) // 32 if nq <= 64 else (nk + 63) // 64
+        ntiles = (nk + 31) // 32 if nq <= 32 else (nk + 63) // 64
         per_range = 2 * nq * 5 * 4  # batch * heads * n_q * 5 floats
         d = L.streamkl_fwd_splitk_default_splits(ctypes.byref(p))
         assert 1 <= d <= ntiles

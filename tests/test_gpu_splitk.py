@@ -22,7 +22,8 @@ SHAPES = [
     (1, 2, 100, 257, 128, False),
     (1, 1, 70, 70, 64, True),
     (1, 32, 16, 65536, 128, False),
-    # more than 64 query rows: ranges run as blocks of the LDS-staged forward kernel
+    (1, 2, 32, 3000, 128, True),
+    # more than 32 query rows: ranges run as blocks of the LDS-staged forward kernel
     (1, 2, 300, 1000, 128, True),
     (2, 2, 513, 777, 64, False),
     (1, 3, 65, 2000, 128, False),
@@ -63,9 +64,10 @@ def test_splitk_matches_oracle(shape, recipe):
             assert_rows_close(to_np(a), to_np(b), tag + what + " vs one-pass")
 
 
-def test_splitk_deterministic_and_ignores_workspace_contents():
-    print("splitk determinism", flush=True)
-    w, d, r = make((1, 4, 9, 3000, 128, False), "perturb")
+@pytest.mark.parametrize("nq", [9, 100])
+def test_splitk_deterministic_and_ignores_workspace_contents(nq):
+    print(f"splitk determinism nq={nq}", flush=True)
+    w, d, r = make((1, 4, nq, 3000, 128, False), "perturb")
     nbytes = skl.streamkl_fwd_splitk_workspace_size(d["q1"], d["k1"], n_splits=5)
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
     a = skl.streamkl_fwd_splitk(d["q1"], d["k1"], d["q2"], d["k2"], n_splits=5,

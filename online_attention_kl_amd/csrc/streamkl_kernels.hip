@@ -150,7 +150,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int r
                                            kBufferWord3);
 }
 
-// voff is range-checked against the resource; soff is added to the address unchecked.
+// Loads 16 bytes at offset voff + soff of the resource. On gfx950 the range check covers the
+// whole offset (vector, scalar and instruction parts) dword by dword: a dword at or past the
+// range reads as 0 (checked with a probe against a resource shorter than its allocation).
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned voff,
                                                unsigned soff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
@@ -174,8 +176,6 @@ struct TileRegs {
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc<ROWS>(base + (long long)row0 * rstride, n_valid - row0, rstride);
     const unsigned off = (threadIdx.x / CPR) * (unsigned)rstride + (threadIdx.x % CPR) * 16u;
-    // the whole offset goes into the vector operand: the range check covers the vector and
-    // instruction offsets but not the scalar one
 #pragma unroll
     for (int i = 0; i < N; ++i)
       if (EVEN || threadIdx.x + i * NT < ROWS * CPR)

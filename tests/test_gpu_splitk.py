@@ -111,3 +111,27 @@ def test_splitk_too_small_workspace_raises():
     with pytest.raises(skl.StreamKLError) as e:
         skl.streamkl_fwd_splitk(d["q1"], d["k1"], d["q2"], d["k2"], n_splits=4, workspace=ws)
     assert e.value.status == 1
+
+
+def test_splitk_blocks_at_64k_keys():
+    """The key-range blocks at the small-N bench shape (32 heads, 512 query rows, 64K keys):
+    every row against the one-pass forward, sampled rows of sampled slices against the oracle."""
+    from oracle.reference import forward_slice
+    print("splitk blocks 32x512x65536", flush=True)
+    B, H, nq, nk, d = 1, 32, 512, 65536, 128
+    w = Workload("splitk_64k", B, H, nq, nk, d, False, (1,), 9, "perturb", sigma=0.5)
+    x = make_inputs(w)
+    dv = {n: dev_bf16(x[n]) for n in ("q1", "k1", "q2", "k2")}
+    assert skl.streamkl_fwd_splitk_default_splits(dv["q1"], dv["k1"]) > 1
+    kl, l1, l2 = skl.streamkl_fwd_splitk(dv["q1"], dv["k1"], dv["q2"], dv["k2"])
+    base = skl.streamkl_fwd(dv["q1"], dv["k1"], dv["q2"], dv["k2"])
+    for a, b, what in zip((kl, l1, l2), base, ("KL", "LSE1", "LSE2")):
+        assert_rows_close(to_np(a), to_np(b), what + " vs one-pass")
+    rng = np.random.default_rng(3)
+    rows = np.array(sorted({0, 255, 256, nq - 1} | set(rng.integers(0, nq, 12).tolist())))
+    for h in (0, 17, H - 1):
+        a = {n: f64(x[n][0, h]) for n in ("q1", "k1", "q2", "k2")}
+        rk, r1, r2 = forward_slice(a["q1"], a["k1"], a["q2"], a["k2"], w.scale, False, rows=rows)
+        assert_rows_close(to_np(kl)[0, h, rows], rk, f"head {h} KL")
+        assert_rows_close(to_np(l1)[0, h, rows], r1, f"head {h} LSE1")
+        assert_rows_close(to_np(l2)[0, h, rows], r2, f"head {h} LSE2")

@@ -464,6 +464,76 @@ def extra_hbm_mode(args):
                                  "backward_settings": [1]}, "rows": rows}), flush=True)
 
 
+def configs_mode(args):
+    """Every workload once: forward + backward of its settings, `--steps` timed steps after
+    `--warmup` (and at least 0.3 s of warmup), HIP events around each step. The two small workloads (tiny_256_d64, nc_4k_d128)
+    are also timed with L2 and the Infinity Cache flushed before every step (a 4 GiB device
+    write outside the timed events), since their inputs otherwise stay cache-resident between
+    steps. One JSON line per (workload, flush)."""
+    import numpy as np
+    import torch
+    import online_attention_kl_amd as skl
+
+    dev = torch.device("cuda:0")
+    flush_buf = torch.empty(1 << 30, dtype=torch.float32, device=dev)
+    order = ["tiny_256_d64", "nc_4k_d128", "causal_16k_sharedk_d128", "causal_64k_d128",
+             "asym_2k_32k_d64"]
+    for name in order:
+        w = WORKLOADS[name]
+        print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+        x = make_inputs(w)
+
+        def up(a):
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        q1, q2, k1 = up(x["q1"]), up(x["q2"]), up(x["k1"])
+        k2 = k1 if x["k2"] is x["k1"] else up(x["k2"])
+        g = torch.from_numpy(x["g"]).to(dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        kl, l1, l2 = (torch.empty((w.batch, w.heads, w.n_q), **f32) for _ in range(3))
+        grads = {s: (torch.empty_like(q1), torch.empty_like(k1)) for s in w.settings}
+
+        def step():
+            skl.streamkl_fwd(q1, k1, q2, k2, causal=w.causal, out=(kl, l1, l2))
+            for s in w.settings:
+                skl.streamkl_bwd_dq(s, q1, k1, q2, k2, l1, l2, kl, g, causal=w.causal,
+                                    out=grads[s][0])
+                skl.streamkl_bwd_dk(s, q1, k1, q2, k2, l1, l2, kl, g, causal=w.causal,
+                                    out=grads[s][1])
+
+        pairs = visible_pairs(w)
+        flop = (4 + 8 * len(w.settings)) * w.head_dim * pairs
+        for flush in ((False, True) if name in ("tiny_256_d64", "nc_4k_d128") else (False,)):
+            # at least --warmup steps and 0.3 s of them, so that short steps do not start timing
+            # before the clocks have risen
+            t_end, n = time.perf_counter() + 0.3, 0
+            while n < args.warmup or time.perf_counter() < t_end:
+                step()
+                torch.cuda.synchronize()
+                n += 1
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for k in range(args.steps):
+                if flush:
+                    flush_buf.fill_(float(k))
+                evs[k][0].record()
+                step()
+                evs[k][1].record()
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+            tf = flop / (ms * 1e-3) / 1e12
+            print(json.dumps({
+                "mode": "configs", "unit": "ms", "steps": args.steps, "warmup": args.warmup,
+                "data": "synthetic", "cache_flushed_before_each_step": flush,
+                "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
+                           "n_q": w.n_q, "n_k": w.n_k, "head_dim": w.head_dim,
+                           "causal": w.causal, "backward_settings": list(w.settings)},
+                "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
+                "pct_bf16_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+        del q1, q2, k1, k2, g, kl, l1, l2, grads
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,6 +550,9 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="time the fp8 e4m3 forward against the bf16 forward on --workload and "
                          "report the effect of the fp8 input rounding on KL and LSE")
+    ap.add_argument("--configs", action="store_true",
+                    help="time forward + backward on every workload (one JSON line each; the "
+                         "two small ones also with caches flushed before every step)")
     ap.add_argument("--extra-hbm", action="store_true",
                     help="device memory beyond inputs and outputs during forward + backward at "
                          "causal N = 16K, 32K, 64K (one JSON line)")
@@ -510,6 +583,9 @@ def main():
         return
     if args.extra_hbm:
         extra_hbm_mode(args)
+        return
+    if args.configs:
+        configs_mode(args)
         return
     w = WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)

@@ -13,7 +13,7 @@ backward 8 d flop per setting (two recomputed contractions and the dQ and dK pro
 two backward kernels are each credited with half of the backward's 8 d (the dQ kernel's
 recomputation of S repeats work the dK kernel also does, and is not counted twice).
 
-Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: this build measures one GPU.
+Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -93,7 +93,7 @@ def write_traffic(fetch_dir: str, write_dir: str, workload: str) -> dict:
         "workload": workload,
         "source_sha256": source_sha(),
         "command": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> -T "
-                   "-f csv -d <repo>/gpurun_out/traffic_<C> -o run -- python3 <repo>/bench.py "
+                   "-f csv -d <out>/traffic_<C> -o run -- python3 <repo>/bench.py "
                    "--steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
         "copy_reference": {"bytes_read": int(gib), "bytes_written": int(gib),
                            "fetch_counter_bytes": fcopy, "write_counter_bytes": wcopy,

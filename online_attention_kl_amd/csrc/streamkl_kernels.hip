@@ -39,11 +39,12 @@
 //    blocks of one slice land on one XCD and share its L2.
 //  * The dK kernel folds the upstream gradient into the exponents (g P = sign(g) 2^(y + log2|g|))
 //    and applies the sign only on tiles that hold a negative g.
-//  * Few query rows: a split-K forward (one wavefront per query block and key range, partial
-//    states merged by a lane group per row), a dQ kernel split over key ranges with a
-//    deterministic sum of the partials, and a fused backward (n_q <= 64) that forms dS once per
-//    key group and uses it for dK and for a per-block partial dQ, reading the keys once; all
-//    three take a workspace from the caller.
+//  * Few query rows: a split-K forward (one wavefront per 32-row query block and key range up
+//    to 32 rows, one block of the LDS-staged forward kernel per 256-row query block and key
+//    range above; partial states merged by a lane group per row), a dQ kernel split over key
+//    ranges with a deterministic sum of the partials, and a fused backward (n_q <= 64) that
+//    forms dS once per key group and uses it for dK and for a per-block partial dQ, reading the
+//    keys once; all three take a workspace from the caller.
 //  * The forward is also built for fp8 e4m3 inputs (v_mfma_scale_f32_32x32x64_f8f6f4, one
 //    dequantisation factor per side), with the same float32 state.
 #include <hip/hip_runtime.h>
@@ -536,8 +537,9 @@ fwd_kernel(const uint8_t* __restrict__ q1, const uint8_t* __restrict__ k1,
 
 // ================================================================ split-K forward
 // With few query rows (decode-like shapes) one block per 256-row query block leaves most of the
-// chip idle. Here every wave has its own work item: a 32-row query block of one slice and one
-// contiguous range of key tiles. The wave reads its keys straight from global memory into MFMA
+// chip idle. Here (up to 32 query rows; above, the key ranges run on fwd_kernel with SPLIT)
+// every wave has its own work item: a 32-row query block of one slice and one contiguous range
+// of key tiles. The wave reads its keys straight from global memory into MFMA
 // operands (no LDS and no barrier: no other wave of the block reads the same keys), runs the
 // forward's online update and writes the partial state of each row (m1, l1, m2, l2, acc; l and
 // acc relative to exp2(c m)) to a workspace laid out [slice][range][5][n_q]. A second kernel

@@ -106,9 +106,9 @@ streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* problem, float desc
  * The keys of every slice are cut into n_splits contiguous ranges of whole key granules. With
  * n_q <= 32 a granule is a 32-key tile and each (slice, 32-row query block, range) is one
  * independent work item of one wavefront that reads its keys straight from memory; with
- * n_q > 32 a granule is a 64-key stage and each (slice, 256-row query block, range) is one
- * block of the LDS-staged forward kernel, so that the query rows of a block share every key
- * read. Either way the work item writes the partial online state (m1, l1, m2, l2, acc) of its
+ * n_q > 32 a granule is one stage of the LDS-staged kernel (64 keys causal, 128 keys without
+ * the mask) and each (slice, 256-row query block, range) is one block of that kernel, so that
+ * the query rows of a block share every key read. Either way the work item writes the partial online state (m1, l1, m2, l2, acc) of its
  * rows to the workspace; a second kernel merges the ranges of each row (the online state of a
  * union of key sets follows from the states of its parts: the larger maximum wins and the other
  * sums are rescaled) and writes kl, lse1, lse2. Results agree with streamkl_fwd to float32

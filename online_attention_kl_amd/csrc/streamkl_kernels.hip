@@ -328,14 +328,20 @@ __device__ __forceinline__ bool non_finite(float x) {
 }
 
 // Forward launch shape: blocks of kFwdWaves waves (32 query rows each), kFwdBlocksPerCU blocks
-// resident per CU, key tiles of 32 * kFwdRB rows, LDS stages of kFwdSB rows (double-buffered).
-// The softmax-style update is VALU-bound and a single wave issues VALU instructions at a
-// fraction of the SIMD's rate, so the shape favours several resident waves per SIMD.
+// resident per CU, key tiles of 32 * kFwdRB rows, LDS stages of fwd_stage_keys rows
+// (double-buffered, one barrier per stage). The softmax-style update is VALU-bound and a single
+// wave issues VALU instructions at a fraction of the SIMD's rate, so the shape favours several
+// resident waves per SIMD.
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBlocksPerCU = 1;
 constexpr int kFwdRB = 1;
-constexpr int kFwdSB = 64;
 constexpr int kFwdThreads = 64 * kFwdWaves;
+// Keys per stage. Without the causal mask 128-key stages (half the barriers) are faster (d = 64:
+// -4.5 %, d = 128: -2 % at the non-causal workloads); with it the waves of a block leave the
+// stage loop at different tiles near the diagonal and the larger stages cost more than the
+// barriers they save (64K causal: +1.6 %), and 32-key stages cost +8 %.
+template <bool CAUSAL>
+constexpr int fwd_stage_keys() { return CAUSAL ? 64 : 128; }
 
 // F: input format (Bf16In or Fp8In). q*/k* point at elements of that format; strides in the
 // Shape are in elements. Side t's logits are scale * sigma_t * Q_t K_t^T.
@@ -351,7 +357,7 @@ fwd_kernel(const uint8_t* __restrict__ q1, const uint8_t* __restrict__ k1,
            float* __restrict__ lse2_out, Shape s, float sigma1, float sigma2,
            float* __restrict__ part = nullptr, int nsplit = 1, int split_keys = 0) {
   constexpr int EB = F::EB, KPER = F::KPER, KS = D / KPER;
-  constexpr int RB = kFwdRB, BK = 32 * RB, SB = kFwdSB, BQ = 32 * kFwdWaves;
+  constexpr int RB = kFwdRB, BK = 32 * RB, SB = fwd_stage_keys<CAUSAL>(), BQ = 32 * kFwdWaves;
   constexpr int NKT = SHARED_K ? 1 : 2;
   static_assert(SB % BK == 0, "a stage holds whole tiles");
   static_assert(!SPLIT || std::is_same<F, Bf16In>::value, "key ranges: bf16 inputs");
@@ -1571,9 +1577,9 @@ void dispatch_fwd(int64_t d, bool causal, bool sk, const Shape& s, const void* q
 // query block per slice (n_q <= 32) every wave is a work item that reads its keys straight
 // from global memory (granules of 32 keys); with more query rows those waves would each read
 // the same keys again, so the work items are blocks of the LDS-staged forward kernel, one
-// 256-row query block by one key range (granules of one 64-key stage). (32 heads, 64K keys:
-// the two paths take the same time at 24-32 rows; at 33-64 rows the blocks take 0.21 ms
-// against 0.25-0.29 ms.)
+// 256-row query block by one key range (granules of one stage: 64 keys causal, 128 without).
+// (32 heads, 64K keys: the two paths take the same time at 24-32 rows; at 33-64 rows the blocks
+// take 0.21 ms against 0.25-0.29 ms.)
 constexpr int kSplitWaveMaxRows = 32;
 
 struct SplitPlan {
@@ -1583,7 +1589,7 @@ struct SplitPlan {
 
 SplitPlan split_plan(const streamkl_problem_t* p, int32_t n_splits) {
   const bool blocks = p->n_q > kSplitWaveMaxRows;
-  const int64_t gran = blocks ? kFwdSB : 32;
+  const int64_t gran = blocks ? (p->causal ? fwd_stage_keys<true>() : fwd_stage_keys<false>()) : 32;
   // with the top-left causal mask no row sees a key past n_q - 1
   const int64_t nvis = p->causal && p->n_q < p->n_k ? p->n_q : p->n_k;
   const int64_t ngran = (nvis + gran - 1) / gran;

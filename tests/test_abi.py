@@ -132,9 +132,9 @@ def test_splitk_plan_and_workspace_size():
                    (512, 65536), (2000, 1000)):
         p = good_problem()
         p.n_q, p.n_k = nq, nk
-        # key granules of a range: 32 keys for wave work items (n_q <= 32), else one 64-key
-        # stage of the LDS-staged kernel
-        ntiles = (nk + 31) // 32 if nq <= 32 else (nk + 63) // 64
+        # key granules of a range: 32 keys for wave work items (n_q <= 32), else one stage of
+        # the LDS-staged kernel (128 keys without the causal mask; good_problem is non-causal)
+        ntiles = (nk + 31) // 32 if nq <= 32 else (nk + 127) // 128
         per_range = 2 * nq * 5 * 4  # batch * heads * n_q * 5 floats
         d = L.streamkl_fwd_splitk_default_splits(ctypes.byref(p))
         assert 1 <= d <= ntiles

@@ -31,6 +31,18 @@ from workloads import WORKLOADS, bf16_bits_to_f32, make_inputs, visible_pairs  #
 
 METRIC = "StreamKL fwd+bwd TFLOP/s and % bf16 MFMA peak, H=32 N=64K d=128 causal"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+# Vector ALU issue slots per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one unpacked fp32
+# operation per lane and slot; the published 157.3 TFLOP/s fp32 vector peak counts packed FMAs
+# as 4 flops). An exp2 counts as 2 slots: a probe issuing only v_exp_f32 took 2.3 times as long
+# per wave instruction as one issuing only FMAs (2 waves per SIMD), i.e. half the fp32 rate.
+PEAK_VALU_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+EXP2_SLOTS = 2
+# The method's own element-wise work per visible (query, key) pair, in (fp32 ops, exp2):
+# forward: 2 FMAs for the exponents, the l1 and l2 sums, the logit difference and the acc FMA,
+# and P1, P2; setting 1 backward kernel: 2 FMAs for the exponents, P2 - P1 and half a bf16 pair
+# conversion, and P1, P2; setting 2: the exponent FMA, the logit difference, the log-ratio FMA,
+# the product with P1 and half a conversion, and P1.
+VALU_WORK = {"fwd": (6.0, 2), "bwd1": (3.5, 2), "bwd2": (4.5, 1)}
 KERNEL_SOURCE = os.path.join(ROOT, "online_attention_kl_amd", "csrc", "streamkl_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -464,6 +476,23 @@ def extra_hbm_mode(args):
                                  "backward_settings": [1]}, "rows": rows}), flush=True)
 
 
+def valu_roofline(kms, pairs):
+    """The vector-ALU roofline of each kernel beside the MFMA one: the method's element-wise work
+    per pair (VALU_WORK, exp2 weighted by EXP2_SLOTS) over the kernel time, against
+    PEAK_VALU_TSLOTS. `frac` is the share of the kernel time that this work alone would take at
+    peak; the kernels' extra instructions (addressing, staging, masks) are not counted."""
+    out = {}
+    for name, ms in kms.items():
+        kind = "fwd" if name == "fwd_kernel" else ("bwd1" if name.endswith("_s1") else "bwd2")
+        ops, ex = VALU_WORK[kind]
+        slots = pairs * (ops + EXP2_SLOTS * ex)
+        achieved = slots / (ms * 1e-3) / 1e12
+        out[name] = {"bound": "alu", "slots_per_pair": ops + EXP2_SLOTS * ex,
+                     "achieved": round(achieved, 2), "peak": round(PEAK_VALU_TSLOTS, 2),
+                     "unit": "Tslot/s", "frac": round(achieved / PEAK_VALU_TSLOTS, 4)}
+    return out
+
+
 def configs_mode(args):
     """Every workload once: forward + backward of its settings, `--steps` timed steps after
     `--warmup` (and at least 0.3 s of warmup), HIP events around each step. The two small workloads (tiny_256_d64, nc_4k_d128)
@@ -703,6 +732,7 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_for(dom, w.name),
         },
+        "valu_roofline": valu_roofline(kms, pairs),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a host sample", file=sys.stderr, flush=True)

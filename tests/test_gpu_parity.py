@@ -27,6 +27,8 @@ SHAPES = [
     (1, 1, 700, 300, 64, True),
     (1, 1, 129, 1024, 128, False),
     (1, 3, 384, 384, 128, False),
+    # many slices: the block -> (slice, row block) mapping over 128 slices
+    (8, 16, 70, 90, 64, True),
 ]
 
 

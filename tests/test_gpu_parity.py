@@ -137,6 +137,33 @@ def test_identical_inputs_give_exact_zeros(causal):
     assert torch.all(dq == 0) and torch.all(dk == 0)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_give_uniform_rows(causal):
+    """Q1 = Q2 = 0: every visible logit is 0, so both distributions are uniform over the row's
+    visible keys: LSE = log(n_visible) (n_k, or min(i + 1, n_k) with the causal mask), KL = 0
+    and every gradient vanishes. Also Q1 = 0 against a random Q2, against the oracle (the KL of
+    a uniform row to P2)."""
+    announce(f"zero queries causal={causal}")
+    w, d, r = make((1, 2, 300, 257, 64, causal), "perturb")
+    z = torch.zeros_like(d["q1"])
+    kl, l1, l2 = skl.streamkl_fwd(z, d["k1"], z, d["k2"], causal=causal)
+    nvis = np.minimum(np.arange(300) + 1, 257) if causal else np.full(300, 257)
+    ref = np.broadcast_to(np.log(nvis.astype(np.float64)), (1, 2, 300))
+    assert_rows_close(to_np(l1), ref, "LSE1 of uniform rows")
+    assert_rows_close(to_np(l2), ref, "LSE2 of uniform rows")
+    assert torch.all(kl == 0)
+    for dq, dk in (skl.streamkl_bwd_fixP1(z, d["k1"], z, d["k2"], l1, l2, d["g"], causal=causal),
+                   skl.streamkl_bwd_fixP2(z, d["k1"], z, d["k2"], l1, l2, kl, d["g"],
+                                          causal=causal)):
+        assert torch.all(dq == 0) and torch.all(dk == 0)
+    rz = np.zeros_like(r["q1"])
+    kl, l1, l2 = skl.streamkl_fwd(z, d["k1"], d["q2"], d["k2"], causal=causal)
+    rk, r1, r2 = oracle.forward(rz, r["k1"], r["q2"], r["k2"], w.scale, causal)
+    assert_rows_close(to_np(kl), rk, "KL(uniform || P2)")
+    assert_rows_close(to_np(l1), r1, "LSE1 (uniform)")
+    assert_rows_close(to_np(l2), r2, "LSE2")
+
+
 def test_forward_is_deterministic():
     announce("determinism")
     w, d, r = make((1, 4, 1000, 1000, 128, True), "perturb")

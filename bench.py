@@ -165,6 +165,18 @@ def summarize_counters(dirs) -> str:
     return "\n".join(lines)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, target_s: float):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload: blocks of 256
     query rows spread evenly over the row range of several slices, forward plus the workload's
@@ -212,7 +224,7 @@ def cpu_baseline(w, x, target_s: float):
     secs = time.perf_counter() - t0
     flop = pairs * w.head_dim * (4 + 8 * len(w.settings))
     return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
-            "seconds": round(secs, 2),
+            "cpu_model": cpu_model(), "seconds": round(secs, 2),
             "sample": f"{rounds} rounds x {workers} slices x 256 query rows (row blocks spread "
                       f"over the range), forward + backward setting(s) {list(w.settings)} "
                       f"restricted to those rows, fp64 numpy, {pairs} visible pairs"}
@@ -262,7 +274,7 @@ def small_nq(args):
             wsb = torch.empty(max(16, skl.streamkl_bwd_fused_workspace_size(q1, k1)),
                               dtype=torch.uint8, device=dev)
         fns = {
-            "fwd_one_pass": lambda: skl.streamkl_fwd(q1, k1, q2, k2, out=out),
+            "fwd_one_pass": lambda: skl.streamkl_fwd_one_pass(q1, k1, q2, k2, out=out),
             "fwd_split_k": lambda: skl.streamkl_fwd_splitk(q1, k1, q2, k2, workspace=wsf, out=out),
             "dq_one_kernel": lambda: skl.streamkl_bwd_dq(1, q1, k1, q2, k2, l1, l2, kl, g, out=dq),
             "dq_split": lambda: skl.streamkl_bwd_dq_splitk(1, q1, k1, q2, k2, l1, l2, kl, g,
@@ -272,6 +284,14 @@ def small_nq(args):
         if fused:
             fns["bwd_fused"] = lambda: skl.streamkl_bwd_fused(1, q1, k1, q2, k2, l1, l2, None, g,
                                                               workspace=wsb, out=(dq, dk))
+        # the adaptive entry points (kernels chosen by the library from the sizes)
+        wsa_f = torch.empty(max(16, skl.streamkl_fwd_workspace_size(q1, k1)), dtype=torch.uint8,
+                            device=dev)
+        wsa_b = torch.empty(max(16, skl.streamkl_bwd_workspace_size(q1, k1)), dtype=torch.uint8,
+                            device=dev)
+        fns["fwd_auto"] = lambda: skl.streamkl_fwd(q1, k1, q2, k2, out=out, workspace=wsa_f)
+        fns["bwd_auto"] = lambda: skl.streamkl_bwd_fixP1(q1, k1, q2, k2, l1, l2, g, out=(dq, dk),
+                                                         workspace=wsa_b)
         ms = {}
         for name, fn in fns.items():
             for _ in range(args.warmup):
@@ -292,6 +312,13 @@ def small_nq(args):
         tfs = flops / (ms["fwd_split_k"] * 1e-3) / 1e12
         kern = ("fwd_split_kernel" if nq <= 32 else "fwd_kernel (key ranges)") + \
             " + fwd_merge_kernel"
+        bwd_manual = {"one_kernel": ms["dq_one_kernel"] + ms["dk"],
+                      "split_dq": ms["dq_split"] + ms["dk"]}
+        if fused:
+            bwd_manual["fused"] = ms["bwd_fused"]
+        best_b = min(bwd_manual, key=bwd_manual.get)
+        best_f = "split_k" if ms["fwd_split_k"] < ms["fwd_one_pass"] else "one_pass"
+        best_fms = min(ms["fwd_split_k"], ms["fwd_one_pass"])
         if fbytes / 8.0e12 >= flops / (PEAK_BF16_TFLOPS * 1e12):
             roof = {"kernel": kern, "bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0,
                     "unit": "GB/s", "frac": round(gbs / 8000.0, 4), "traffic": None}
@@ -316,6 +343,10 @@ def small_nq(args):
                             round((ms["dq_one_kernel"] + ms["dk"]) / ms["bwd_fused"], 2)
                             if fused else None)},
             "roofline": roof,
+            "adaptive": {"fwd_best_manual": best_f,
+                         "fwd_auto_vs_best_manual": round(ms["fwd_auto"] / best_fms, 3),
+                         "bwd_best_manual": best_b,
+                         "bwd_auto_vs_best_manual": round(ms["bwd_auto"] / bwd_manual[best_b], 3)},
         }
         print(json.dumps(line), flush=True)
 
@@ -522,13 +553,21 @@ def configs_mode(args):
         kl, l1, l2 = (torch.empty((w.batch, w.heads, w.n_q), **f32) for _ in range(3))
         grads = {s: (torch.empty_like(q1), torch.empty_like(k1)) for s in w.settings}
 
+        # the adaptive entry points, with their workspaces allocated once
+        wsf = torch.empty(max(16, skl.streamkl_fwd_workspace_size(q1, k1, causal=w.causal)),
+                          dtype=torch.uint8, device=dev)
+        wsb = torch.empty(max(16, skl.streamkl_bwd_workspace_size(q1, k1, causal=w.causal)),
+                          dtype=torch.uint8, device=dev)
+
         def step():
-            skl.streamkl_fwd(q1, k1, q2, k2, causal=w.causal, out=(kl, l1, l2))
+            skl.streamkl_fwd(q1, k1, q2, k2, causal=w.causal, out=(kl, l1, l2), workspace=wsf)
             for s in w.settings:
-                skl.streamkl_bwd_dq(s, q1, k1, q2, k2, l1, l2, kl, g, causal=w.causal,
-                                    out=grads[s][0])
-                skl.streamkl_bwd_dk(s, q1, k1, q2, k2, l1, l2, kl, g, causal=w.causal,
-                                    out=grads[s][1])
+                if s == 1:
+                    skl.streamkl_bwd_fixP1(q1, k1, q2, k2, l1, l2, g, causal=w.causal,
+                                           out=grads[s], workspace=wsb)
+                else:
+                    skl.streamkl_bwd_fixP2(q1, k1, q2, k2, l1, l2, kl, g, causal=w.causal,
+                                           out=grads[s], workspace=wsb)
 
         pairs = visible_pairs(w)
         flop = (4 + 8 * len(w.settings)) * w.head_dim * pairs
@@ -650,6 +689,12 @@ def main():
     torch.cuda.reset_peak_memory_stats(dev)
 
     names = ["fwd_kernel"] + [f"{k}_kernel_s{s}" for s in w.settings for k in ("dq", "dk")]
+    # at this workload the adaptive entry points run exactly these kernels (one-pass forward;
+    # one-kernel dQ and dK), which are launched one by one here to time each of them
+    if skl.streamkl_fwd_workspace_size(q1, k1, causal=w.causal) != 0 or \
+            skl.streamkl_bwd_workspace_size(q1, k1, causal=w.causal) != 0:
+        raise SystemExit(f"{w.name}: the adaptive plan is not one-pass forward + one-kernel dQ "
+                         "and dK; time it with --configs")
 
     def step(ev=None):
         i = 0
@@ -660,7 +705,7 @@ def main():
                 ev[i].record()
             i += 1
         mark()
-        skl.streamkl_fwd(q1, k1, q2, k2, causal=w.causal, out=(kl, l1, l2))
+        skl.streamkl_fwd_one_pass(q1, k1, q2, k2, causal=w.causal, out=(kl, l1, l2))
         mark()
         for s in w.settings:
             skl.streamkl_bwd_dq(s, q1, k1, q2, k2, l1, l2, kl, g, causal=w.causal, out=grads[s][0])

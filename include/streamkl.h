@@ -25,7 +25,12 @@
  *    from a thread-local error message, so calls from several host threads are safe.
  *  - Validation happens before anything is enqueued: an invalid call returns an error status
  *    and touches no buffer. A launch failure returns STREAMKL_ERROR_HIP; outputs are then
- *    undefined. Non-finite inputs are not checked; they propagate.
+ *    undefined.
+ *  - Non-finite inputs (NaN, infinity) are not checked. Every output that depends on one has an
+ *    unspecified value (the kernels are built without NaN semantics, so a NaN is not
+ *    guaranteed to reach the output); outputs that do not depend on it are unaffected. Per
+ *    query row: kl, lse1, lse2 and the dQ row of query i depend only on row i of q1 / q2 and on
+ *    every key; each dK row depends on every query row.
  *  - Inputs may alias each other (k2 == k1 and/or q2 == q1 are allowed and k2 == k1 is
  *    detected and loads the shared tensor once). Outputs must not overlap any input or each
  *    other (STREAMKL_ERROR_INVALID_VALUE).
@@ -62,7 +67,8 @@ typedef struct {
 
 /*
  * Forward pass (gist.science/pt "Metodologia" section 1, "Formulacao Online"; saved state per
- * section 2, "Estado Salvo").
+ * section 2, "Estado Salvo"; the split-K variant for small N_Q per section 3 and its gain under
+ * "Resultados Experimentais", ablation).
  *
  * Streams key tiles through on-chip memory and keeps per query row the running maxima m1, m2,
  * the running sums of exponentials l1, l2 and the P1-weighted logit-difference accumulator acc,
@@ -74,12 +80,37 @@ typedef struct {
  * logit of its first tile by more than about 88 / (scale * log2(e)) in unscaled units, i.e.
  * 2^7 in exp2 units) is recomputed with the maxima raised on every tile.
  * Outputs (device, float32, contiguous [batch, heads, n_q], overwritten): kl, lse1, lse2.
- * The result is bitwise deterministic, and kl is exactly 0 where (Q1, K1) and (Q2, K2) hold
+ *
+ * Adaptive: the kernels are chosen from the sizes alone. When few query blocks leave the chip
+ * idle (streamkl_fwd_splitk_default_splits(problem) > 1: at most 256 work items unsplit) the
+ * keys of every slice are cut into ranges, each range's partial online state goes to the
+ * workspace and a second kernel merges them (as streamkl_fwd_splitk with n_splits = 0);
+ * otherwise one pass (streamkl_fwd_one_pass) with no workspace. Either way the result is
+ * bitwise deterministic for given sizes, and kl is exactly 0 where (Q1, K1) and (Q2, K2) hold
  * identical values.
+ * workspace: device memory of at least streamkl_fwd_workspace_size(problem) bytes, 16-byte
+ *   aligned, owned by the caller, overlapping no input or output; may be NULL when that size is
+ *   0 (always the case at the large shapes, e.g. 32 heads x 64K rows). Contents on entry are
+ *   ignored and on return unspecified.
+ * Errors: STREAMKL_ERROR_INVALID_VALUE / _NOT_SUPPORTED for invalid or unsupported problems,
+ *   pointers or overlaps and for a too small, NULL or misaligned workspace when one is needed.
  */
+/* Workspace bytes streamkl_fwd needs for this problem (0 when it runs one pass, and for a NULL
+ * problem or sizes < 1). */
+size_t streamkl_fwd_workspace_size(const streamkl_problem_t* problem);
 streamkl_status_t streamkl_fwd(const streamkl_problem_t* problem,
                                const void* q1, const void* k1, const void* q2, const void* k2,
-                               float* kl, float* lse1, float* lse2, hipStream_t stream);
+                               float* kl, float* lse1, float* lse2, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The one-pass forward kernel alone, whatever the sizes (no workspace): one block per 256 query
+ * rows of a slice streams every visible key tile. Same outputs as streamkl_fwd; for callers that
+ * want this kernel (or time it) at shapes where streamkl_fwd would split the keys.
+ */
+streamkl_status_t streamkl_fwd_one_pass(const streamkl_problem_t* problem, const void* q1,
+                                        const void* k1, const void* q2, const void* k2,
+                                        float* kl, float* lse1, float* lse2, hipStream_t stream);
 
 /*
  * Forward pass with OCP fp8 e4m3 inputs (mixed precision for the two Q K^T contractions,
@@ -139,6 +170,22 @@ streamkl_status_t streamkl_fwd_splitk(const streamkl_problem_t* problem,
                                       hipStream_t stream);
 
 /*
+ * Workspace of the backward entry points streamkl_bwd_fixP1 / _fixP2 (gist.science/pt
+ * "Metodologia" section 2, kernel fusion: the dQ buffer of the fused variant; "Resultados
+ * Experimentais", ablation: the choice between fused and separate kernels adapts to N_Q).
+ * Both settings choose their kernels from the sizes alone, the same way:
+ *   - n_q <= 64: the fused single visit (as streamkl_bwd_fused): dS formed once per key group
+ *     for both gradients, per-key-block partial dQ in the workspace, summed in a fixed order;
+ *   - else, while the one-kernel dQ pass has fewer than 256 blocks: dQ with the keys split into
+ *     ranges (as streamkl_bwd_dq_splitk with n_splits = 0, partials in the workspace) and the
+ *     one-kernel dK pass;
+ *   - else: the one-kernel dQ and dK passes (streamkl_bwd_dq + streamkl_bwd_dk), no workspace.
+ * Returns the bytes that choice needs (0 for the last case, e.g. 32 heads x 64K rows; 0 for a
+ * NULL problem, sizes < 1 or an unsupported head_dim).
+ */
+size_t streamkl_bwd_workspace_size(const streamkl_problem_t* problem);
+
+/*
  * Backward, setting 1: P1 fixed (stop-gradient), P2 free - standard distillation
  * (gist.science/pt "Metodologia" section 2, "Configuracao 1").
  *
@@ -149,12 +196,20 @@ streamkl_status_t streamkl_fwd_splitk(const streamkl_problem_t* problem,
  * streamkl_fwd for the same inputs. grad_kl holds g_i (any real values).
  * Outputs dq2 [batch, heads, n_q, head_dim] and dk2 [batch, heads, n_k, head_dim]: device
  * bfloat16, contiguous, overwritten; accumulation is float32. With k2 == k1, dk2 is the
- * gradient through the student side only. Deterministic (no atomics).
+ * gradient through the student side only. The kernels are chosen as described at
+ * streamkl_bwd_workspace_size; no path uses atomics and every sum has a fixed order, so the
+ * result is bitwise deterministic for given sizes.
+ * workspace: at least streamkl_bwd_workspace_size(problem) bytes of device memory, 16-byte
+ *   aligned, owned by the caller, overlapping no input or output; may be NULL when that size
+ *   is 0. Contents on entry ignored, on return unspecified.
+ * Errors: STREAMKL_ERROR_INVALID_VALUE / _NOT_SUPPORTED for invalid or unsupported problems,
+ *   pointers or overlaps and for a too small, NULL or misaligned workspace when one is needed.
  */
 streamkl_status_t streamkl_bwd_fixP1(const streamkl_problem_t* problem,
                                      const void* q1, const void* k1, const void* q2,
                                      const void* k2, const float* lse1, const float* lse2,
                                      const float* grad_kl, void* dq2, void* dk2,
+                                     void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
 /*
@@ -164,20 +219,22 @@ streamkl_status_t streamkl_bwd_fixP1(const streamkl_problem_t* problem,
  * Forms dS1 = g_i * P1 * (log P1 - log P2 - KL[i]) with the log-ratio taken from logit
  * differences and saved LSEs, (S1 - lse1) - (S2 - lse2), never from the log of a probability,
  * and writes  dq1 = scale * dS1 K1,  dk1 = scale * dS1^T Q1.
- * kl: the forward's saved KL, device float32 contiguous [batch, heads, n_q]; other arguments
- * as in streamkl_bwd_fixP1. Outputs dq1, dk1: device bfloat16, contiguous, overwritten.
+ * kl: the forward's saved KL, device float32 contiguous [batch, heads, n_q]; other arguments,
+ * the kernel choice, the workspace and the errors as in streamkl_bwd_fixP1. Outputs dq1, dk1:
+ * device bfloat16, contiguous, overwritten.
  */
 streamkl_status_t streamkl_bwd_fixP2(const streamkl_problem_t* problem,
                                      const void* q1, const void* k1, const void* q2,
                                      const void* k2, const float* lse1, const float* lse2,
                                      const float* kl, const float* grad_kl, void* dq1, void* dk1,
+                                     void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
 /*
  * The two halves of a backward call, one kernel each, for callers that need only one gradient
  * (for example when K is frozen and only dQ is wanted) or that time the kernels separately.
- * streamkl_bwd_fixP1 = streamkl_bwd_dq + streamkl_bwd_dk with setting = 1, and
- * streamkl_bwd_fixP2 the same with setting = 2 (gist.science/pt "Metodologia" section 2:
+ * streamkl_bwd_dq + streamkl_bwd_dk with setting = 1 is what streamkl_bwd_fixP1 runs at large
+ * sizes, and setting = 2 likewise for streamkl_bwd_fixP2 (gist.science/pt "Metodologia" section 2:
  * dQ accumulates along K, dK along Q; here each runs in its own kernel and neither needs
  * atomics).
  * setting: 1 (P1 fixed; writes dq2 / dk2) or 2 (P2 fixed; writes dq1 / dk1). kl is read only for
@@ -236,8 +293,9 @@ streamkl_status_t streamkl_bwd_dq_splitk(const streamkl_problem_t* problem, int3
  * setting's free side once, and uses it for both products: dK of the group's keys is written
  * directly, and the block's partial dQ (its 128 * G keys) goes to the workspace; a second kernel sums
  * the key blocks' partials in a fixed order and rounds once to bfloat16. The keys are read once
- * instead of once per gradient. No atomics on global memory: the result is deterministic and
- * agrees with streamkl_bwd_fixP1 / _fixP2 to float32 summation order before the rounding.
+ * instead of once per gradient. No atomics: the four waves of a block add their partial dQ in
+ * LDS in wave order, so the result is bitwise deterministic, and agrees with streamkl_bwd_dq /
+ * streamkl_bwd_dk to float32 summation order before the rounding.
  *
  * setting: 1 (P1 fixed; outputs dQ2, dK2, kl unused and may be NULL) or 2 (P2 fixed; outputs
  *   dQ1, dK1, kl required).

@@ -6,15 +6,20 @@ the C ABI declared in include/streamkl.h. Every step of the computation runs in 
 HIP kernels; there is no fallback. If the library has not been built, `lib()` raises.
 
 Functions (names follow the C ABI):
-  streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False)           -> (kl, lse1, lse2)
+  streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False)           -> (kl, lse1, lse2); adaptive
+  streamkl_fwd_workspace_size(q1, k1, ...), streamkl_bwd_workspace_size(q1, k1, ...)
+  streamkl_fwd_one_pass(q1, k1, q2, k2, ...)                        -> (kl, lse1, lse2)
   streamkl_fwd_fp8(q1, k1, q2, k2, descale1=1, descale2=1, ...)   -> (kl, lse1, lse2), fp8 inputs
   streamkl_fwd_splitk(q1, k1, q2, k2, n_splits=0, ...)             -> (kl, lse1, lse2)
   streamkl_fwd_splitk_default_splits(q1, k1, ...), streamkl_fwd_splitk_workspace_size(...)
-  streamkl_bwd_fixP1(q1, k1, q2, k2, lse1, lse2, grad_kl, ...)      -> (dq2, dk2)
-  streamkl_bwd_fixP2(q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...)  -> (dq1, dk1)
+  streamkl_bwd_fixP1(q1, k1, q2, k2, lse1, lse2, grad_kl, ...)      -> (dq2, dk2); adaptive
+  streamkl_bwd_fixP2(q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...)  -> (dq1, dk1); adaptive
   streamkl_bwd_dq(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...) -> dq (one kernel)
   streamkl_bwd_dk(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, ...) -> dk (one kernel)
   streamkl_bwd_dq_splitk(setting, ..., n_splits=0)                 -> dq (key ranges + sum)
+  streamkl_bwd_fused(setting, ...)                                  -> (dq, dk), n_q <= 64
+The adaptive entry points take an optional `workspace` (a uint8 CUDA tensor); when it is needed
+and not given, it is allocated here with PyTorch (the library itself never allocates).
 Inputs are bfloat16 CUDA tensors [B, H, N, d] (the d axis contiguous, any other strides that
 are multiples of 8 elements); kl / lse / grad_kl are float32 [B, H, N_Q].
 """
@@ -29,8 +34,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamkl
 STATUS = {0: "STREAMKL_SUCCESS", 1: "STREAMKL_ERROR_INVALID_VALUE",
           2: "STREAMKL_ERROR_NOT_SUPPORTED", 3: "STREAMKL_ERROR_HIP"}
 
-EXPORTS = ("streamkl_fwd", "streamkl_fwd_fp8", "streamkl_fwd_splitk", "streamkl_fwd_splitk_default_splits",
-           "streamkl_fwd_splitk_workspace_size", "streamkl_bwd_fixP1", "streamkl_bwd_fixP2",
+EXPORTS = ("streamkl_fwd", "streamkl_fwd_workspace_size", "streamkl_fwd_one_pass",
+           "streamkl_fwd_fp8", "streamkl_fwd_splitk", "streamkl_fwd_splitk_default_splits",
+           "streamkl_fwd_splitk_workspace_size", "streamkl_bwd_workspace_size",
+           "streamkl_bwd_fixP1", "streamkl_bwd_fixP2",
            "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_bwd_dq_splitk",
            "streamkl_bwd_dq_splitk_default_splits", "streamkl_bwd_dq_splitk_workspace_size",
            "streamkl_bwd_fused", "streamkl_bwd_fused_workspace_size",
@@ -65,7 +72,13 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L = ctypes.CDLL(p)
     vp, fp = ctypes.c_void_p, ctypes.c_void_p
     pp = ctypes.POINTER(Problem)
-    L.streamkl_fwd.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp]
+    L.streamkl_fwd.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp, ctypes.c_size_t, vp]
+    L.streamkl_fwd_workspace_size.argtypes = [pp]
+    L.streamkl_fwd_workspace_size.restype = ctypes.c_size_t
+    L.streamkl_fwd_one_pass.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp]
+    L.streamkl_fwd_one_pass.restype = ctypes.c_int
+    L.streamkl_bwd_workspace_size.argtypes = [pp]
+    L.streamkl_bwd_workspace_size.restype = ctypes.c_size_t
     L.streamkl_fwd_fp8.argtypes = [pp, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, fp, fp, fp,
                                    vp]
     L.streamkl_fwd_fp8.restype = ctypes.c_int
@@ -76,8 +89,10 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.streamkl_fwd_splitk_default_splits.restype = ctypes.c_int32
     L.streamkl_fwd_splitk_workspace_size.argtypes = [pp, ctypes.c_int32]
     L.streamkl_fwd_splitk_workspace_size.restype = ctypes.c_size_t
-    L.streamkl_bwd_fixP1.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp, vp, vp]
-    L.streamkl_bwd_fixP2.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, fp, vp, vp, vp]
+    L.streamkl_bwd_fixP1.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
+    L.streamkl_bwd_fixP2.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, fp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
     for name in ("streamkl_bwd_dq", "streamkl_bwd_dk"):
         getattr(L, name).argtypes = [pp, ctypes.c_int32, vp, vp, vp, vp, fp, fp, fp, fp, vp, vp]
     L.streamkl_bwd_dq_splitk.argtypes = [pp, ctypes.c_int32, vp, vp, vp, vp, fp, fp, fp, fp, vp,
@@ -147,20 +162,57 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False, out=None):
-    """Per-row KL(P1 || P2), LSE1, LSE2 (float32 [B, H, N_Q])."""
+def _workspace(need, workspace, device):
+    """The caller's workspace tensor (checked) or, when none is given and `need` > 0, a new one.
+    Returns (pointer or None, size in bytes, tensor kept alive by the caller)."""
     import torch
-    _check_inputs(q1, k1, q2, k2)
+    if workspace is None:
+        if need == 0:
+            return None, 0, None
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+
+
+def _fwd_out(q1, out):
+    import torch
     B, H, nq, _ = q1.shape
     if out is None:
         out = tuple(torch.empty((B, H, nq), dtype=torch.float32, device=q1.device)
                     for _ in range(3))
     for n, t in zip(("kl", "lse1", "lse2"), out):
         _rowvec(t, n, (B, H, nq))
+    return out
+
+
+def streamkl_fwd_workspace_size(q1, k1, scale=None, causal=False) -> int:
     p = make_problem(q1, k1, scale, causal)
+    return int(lib().streamkl_fwd_workspace_size(ctypes.byref(p)))
+
+
+def streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False, out=None, workspace=None):
+    """Per-row KL(P1 || P2), LSE1, LSE2 (float32 [B, H, N_Q]); the library picks one pass or the
+    split-K path from the sizes."""
+    _check_inputs(q1, k1, q2, k2)
+    out = _fwd_out(q1, out)
+    p = make_problem(q1, k1, scale, causal)
+    need = int(lib().streamkl_fwd_workspace_size(ctypes.byref(p)))
+    wp, wn, _keep = _workspace(need, workspace, q1.device)
     _check(lib().streamkl_fwd(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
                               k2.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
-                              out[2].data_ptr(), _stream(q1)))
+                              out[2].data_ptr(), wp, wn, _stream(q1)))
+    return out
+
+
+def streamkl_fwd_one_pass(q1, k1, q2, k2, scale=None, causal=False, out=None):
+    """The one-pass forward kernel whatever the sizes (no workspace)."""
+    _check_inputs(q1, k1, q2, k2)
+    out = _fwd_out(q1, out)
+    p = make_problem(q1, k1, scale, causal)
+    _check(lib().streamkl_fwd_one_pass(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(),
+                                       q2.data_ptr(), k2.data_ptr(), out[0].data_ptr(),
+                                       out[1].data_ptr(), out[2].data_ptr(), _stream(q1)))
     return out
 
 
@@ -240,34 +292,46 @@ def _grad_out(q, k, out):
     return out
 
 
-def streamkl_bwd_fixP1(q1, k1, q2, k2, lse1, lse2, grad_kl, scale=None, causal=False, out=None):
-    """Setting 1 (P1 fixed): gradients (dq2, dk2) of sum g_i KL_i, bfloat16."""
+def streamkl_bwd_workspace_size(q1, k1, scale=None, causal=False) -> int:
+    p = make_problem(q1, k1, scale, causal)
+    return int(lib().streamkl_bwd_workspace_size(ctypes.byref(p)))
+
+
+def streamkl_bwd_fixP1(q1, k1, q2, k2, lse1, lse2, grad_kl, scale=None, causal=False, out=None,
+                       workspace=None):
+    """Setting 1 (P1 fixed): gradients (dq2, dk2) of sum g_i KL_i, bfloat16; the library picks
+    the kernels from the sizes."""
     _check_inputs(q1, k1, q2, k2)
     B, H, nq, _ = q1.shape
     for n, t in (("lse1", lse1), ("lse2", lse2), ("grad_kl", grad_kl)):
         _rowvec(t, n, (B, H, nq))
     out = _grad_out(q2, k2, out)
     p = make_problem(q1, k1, scale, causal)
+    need = int(lib().streamkl_bwd_workspace_size(ctypes.byref(p)))
+    wp, wn, _keep = _workspace(need, workspace, q1.device)
     _check(lib().streamkl_bwd_fixP1(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
                                     k2.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
                                     grad_kl.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
-                                    _stream(q1)))
+                                    wp, wn, _stream(q1)))
     return out
 
 
 def streamkl_bwd_fixP2(q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=None, causal=False,
-                       out=None):
-    """Setting 2 (P2 fixed): gradients (dq1, dk1) of sum g_i KL_i, bfloat16."""
+                       out=None, workspace=None):
+    """Setting 2 (P2 fixed): gradients (dq1, dk1) of sum g_i KL_i, bfloat16; the library picks
+    the kernels from the sizes."""
     _check_inputs(q1, k1, q2, k2)
     B, H, nq, _ = q1.shape
     for n, t in (("lse1", lse1), ("lse2", lse2), ("kl", kl), ("grad_kl", grad_kl)):
         _rowvec(t, n, (B, H, nq))
     out = _grad_out(q1, k1, out)
     p = make_problem(q1, k1, scale, causal)
+    need = int(lib().streamkl_bwd_workspace_size(ctypes.byref(p)))
+    wp, wn, _keep = _workspace(need, workspace, q1.device)
     _check(lib().streamkl_bwd_fixP2(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
                                     k2.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
                                     kl.data_ptr(), grad_kl.data_ptr(), out[0].data_ptr(),
-                                    out[1].data_ptr(), _stream(q1)))
+                                    out[1].data_ptr(), wp, wn, _stream(q1)))
     return out
 
 

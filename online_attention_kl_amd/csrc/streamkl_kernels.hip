@@ -1294,7 +1294,6 @@ fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
     const bool any_neg = __any(neg);
     if (q == 0) qneg = any_neg ? 1 : 0;
   }
-  for (int i = threadIdx.x; i < MQ * D; i += kFusedThreads) dqacc[i] = 0.f;
   __syncthreads();
   const bool signed_q = qneg != 0;
   const float c = s.scale * kLog2e;
@@ -1430,17 +1429,26 @@ fused_bwd_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k
       fetch(grp + 1, f1, f2);
     }
   }
-  // the block's partial dQ: the waves' accumulators summed in LDS, then written times scale
+  // the block's partial dQ: the waves' accumulators summed in LDS in wave order (wave 0
+  // stores, waves 1, 2, 3 add in turn, one barrier per turn), so the float32 sum has a fixed
+  // order and the result is the same on every run; then written times scale
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    if (qt >= nqt) continue;
+  for (int turn = 0; turn < kFusedWaves; ++turn) {
+    if (w == turn) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int qt = 0; qt < NQT; ++qt) {
+        if (qt >= nqt) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        atomicAdd(&dqacc[(qt * 32 + acc_row(r, h)) * D + nb * 32 + col], pq[qt][nb][r]);
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float* a = &dqacc[(qt * 32 + acc_row(r, h)) * D + nb * 32 + col];
+            *a = turn == 0 ? pq[qt][nb][r] : *a + pq[qt][nb][r];
+          }
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
   float* dst = part + ((long long)kb * s.bh + slice) * s.nq * D;
   for (int i = threadIdx.x * 4; i < s.nq * D; i += kFusedThreads * 4) {
     float4 v = *reinterpret_cast<const float4*>(&dqacc[i]);
@@ -1803,13 +1811,41 @@ void dispatch_fused(int64_t d, bool causal, bool sk, const Shape& s, int groups,
 #undef SKL_FUS
 }
 
+// Which kernels a backward call runs.
+enum class BwdPath {
+  kSeparate,  // dq_kernel + dk_kernel (no workspace)
+  kSplitDq,   // dq_kernel over key ranges + dq_reduce_kernel, and dk_kernel
+  kFused,     // fused_bwd_kernel + dq_reduce_kernel (n_q <= kFusedMaxQ)
+};
+
+struct BwdPlan {
+  BwdPath path;
+  DqSplitPlan dq;  // key ranges of the dQ kernel (kSplitDq)
+  size_t workspace;
+};
+
+// The adaptive choice of the plain backward entry points, from the problem's sizes alone.
+// With few query rows the keys dominate the traffic and one key-major pass that forms dS once
+// for both gradients is fastest (the fused path: 1.6-1.7x the split pair at n_q <= 64, 32 heads,
+// 64K keys); above that, while the one-kernel dQ has fewer than 256 blocks, its keys are split
+// into ranges; otherwise the two one-kernel passes, which need no workspace.
+BwdPlan bwd_auto_plan(const streamkl_problem_t* p) {
+  if (p->n_q <= kFusedMaxQ) return {BwdPath::kFused, {1, 0}, fused_workspace_bytes(p)};
+  const DqSplitPlan dq = dq_split_plan(p, 0);
+  if (dq.nsplit > 1) return {BwdPath::kSplitDq, dq, dq_split_workspace_bytes(p, dq.nsplit)};
+  return {BwdPath::kSeparate, {1, 0}, 0};
+}
+
+// How the caller chose the kernels: the adaptive plan, one gradient's one-kernel pass, the key
+// split dQ with a requested range count, or the fused pass.
+enum class BwdMode { kAuto, kOneKernel, kSplitDq, kFused };
+
 streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const void* q1,
                              const void* k1, const void* q2, const void* k2, const float* lse1,
                              const float* lse2, const float* kl, const float* grad_kl, void* dq,
                              void* dk, bool want_dq, bool want_dk, hipStream_t stream,
-                             const char* what, const int32_t* dq_splits = nullptr,
-                             void* workspace = nullptr, size_t workspace_bytes = 0,
-                             bool fused = false) {
+                             const char* what, BwdMode mode, int32_t dq_splits = 0,
+                             void* workspace = nullptr, size_t workspace_bytes = 0) {
   Shape s;
   streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
   if (st != STREAMKL_SUCCESS) return st;
@@ -1817,12 +1853,19 @@ streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const voi
   if (!lse1 || !lse2 || !grad_kl || (setting == 2 && !kl))
     return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": NULL lse / kl / grad pointer");
   const int64_t n = p->batch * p->heads * p->n_q;
-  if (fused && p->n_q > kFusedMaxQ)
+  if (mode == BwdMode::kFused && p->n_q > kFusedMaxQ)
     return fail(STREAMKL_ERROR_NOT_SUPPORTED,
                 std::string(what) + ": n_q must be at most " + std::to_string(kFusedMaxQ));
-  DqSplitPlan plan = {1, 0};
-  if (dq_splits) plan = dq_split_plan(p, *dq_splits);
-  const size_t need = fused ? fused_workspace_bytes(p) : dq_split_workspace_bytes(p, plan.nsplit);
+  BwdPlan plan = {BwdPath::kSeparate, {1, 0}, 0};
+  if (mode == BwdMode::kAuto) {
+    plan = bwd_auto_plan(p);
+  } else if (mode == BwdMode::kFused) {
+    plan = {BwdPath::kFused, {1, 0}, fused_workspace_bytes(p)};
+  } else if (mode == BwdMode::kSplitDq) {
+    const DqSplitPlan dq = dq_split_plan(p, dq_splits);
+    if (dq.nsplit > 1) plan = {BwdPath::kSplitDq, dq, dq_split_workspace_bytes(p, dq.nsplit)};
+  }
+  const size_t need = plan.workspace;
   if (workspace_bytes < need)
     return fail(STREAMKL_ERROR_INVALID_VALUE,
                 std::string(what) + ": workspace too small (" + std::to_string(workspace_bytes) +
@@ -1839,41 +1882,104 @@ streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const voi
   for (int i = 0; i < n_out; ++i)
     for (const Span& v : vin)
       if (overlaps(outs[i], v)) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": output overlaps an input");
-  if (plan.nsplit > 1 &&
-      (int64_t)plan.nsplit * p->batch * p->heads * ((p->n_q + 255) / 256) >= ((int64_t)1 << 31))
+  if (plan.path == BwdPath::kSplitDq &&
+      (int64_t)plan.dq.nsplit * p->batch * p->heads * ((p->n_q + 255) / 256) >= ((int64_t)1 << 31))
     return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": grid too large");
-  if (fused && fused_key_blocks(p) * p->batch * p->heads >= ((int64_t)1 << 31))
+  if (plan.path == BwdPath::kFused && fused_key_blocks(p) * p->batch * p->heads >= ((int64_t)1 << 31))
     return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": grid too large");
   (void)hipGetLastError();
   void* dqp = want_dq ? dq : nullptr;
   void* dkp = want_dk ? dk : nullptr;
-  if (fused) {
+  const bool causal = p->causal != 0, sk = k1 == k2;
+  if (plan.path == BwdPath::kFused) {
     float* part = static_cast<float*>(workspace);
     if (setting == 1)
-      dispatch_fused<1>(p->head_dim, p->causal != 0, k1 == k2, s, fused_groups(p), q1, k1, q2,
-                        k2, lse1, lse2, nullptr, grad_kl, dq, dk, part, stream);
+      dispatch_fused<1>(p->head_dim, causal, sk, s, fused_groups(p), q1, k1, q2, k2, lse1, lse2,
+                        nullptr, grad_kl, dq, dk, part, stream);
     else
-      dispatch_fused<2>(p->head_dim, p->causal != 0, k1 == k2, s, fused_groups(p), q1, k1, q2,
-                        k2, lse1, lse2, kl, grad_kl, dq, dk, part, stream);
+      dispatch_fused<2>(p->head_dim, causal, sk, s, fused_groups(p), q1, k1, q2, k2, lse1, lse2,
+                        kl, grad_kl, dq, dk, part, stream);
     return check_launch(what);
   }
-  if (dqp && plan.nsplit > 1) {
+  if (dqp && plan.path == BwdPath::kSplitDq) {
     float* part = static_cast<float*>(workspace);
     if (setting == 1)
-      dispatch_dq_split<1>(p->head_dim, p->causal != 0, k1 == k2, s, plan, q1, k1, q2, k2, lse1,
-                           lse2, nullptr, grad_kl, dqp, part, stream);
+      dispatch_dq_split<1>(p->head_dim, causal, sk, s, plan.dq, q1, k1, q2, k2, lse1, lse2,
+                           nullptr, grad_kl, dqp, part, stream);
     else
-      dispatch_dq_split<2>(p->head_dim, p->causal != 0, k1 == k2, s, plan, q1, k1, q2, k2, lse1,
-                           lse2, kl, grad_kl, dqp, part, stream);
+      dispatch_dq_split<2>(p->head_dim, causal, sk, s, plan.dq, q1, k1, q2, k2, lse1, lse2, kl,
+                           grad_kl, dqp, part, stream);
     dqp = nullptr;
   }
   if (!dqp && !dkp) return check_launch(what);
   if (setting == 1)
-    dispatch_bwd<1>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, lse1, lse2, nullptr,
-                    grad_kl, dqp, dkp, stream);
+    dispatch_bwd<1>(p->head_dim, causal, sk, s, q1, k1, q2, k2, lse1, lse2, nullptr, grad_kl, dqp,
+                    dkp, stream);
   else
-    dispatch_bwd<2>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, lse1, lse2, kl,
-                    grad_kl, dqp, dkp, stream);
+    dispatch_bwd<2>(p->head_dim, causal, sk, s, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, dqp, dkp,
+                    stream);
+  return check_launch(what);
+}
+
+// The forward's adaptive choice: the split-K path when its plan cuts the keys into more than
+// one range (few query blocks for the chip), else the one-pass kernel with no workspace.
+bool sizes_ok(const streamkl_problem_t* p) {
+  return p && p->batch >= 1 && p->heads >= 1 && p->n_q >= 1 && p->n_k >= 1;
+}
+
+size_t fwd_auto_workspace(const streamkl_problem_t* p) {
+  const SplitPlan plan = split_plan(p, 0);
+  return plan.nsplit > 1 ? split_workspace_bytes(p, plan.nsplit) : 0;
+}
+
+streamkl_status_t fwd_splitk_common(const streamkl_problem_t* p, const void* q1, const void* k1,
+                                    const void* q2, const void* k2, float* kl, float* lse1,
+                                    float* lse2, const SplitPlan& plan, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream, const char* what) {
+  Shape s;
+  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
+  if (st != STREAMKL_SUCCESS) return st;
+  const size_t need = split_workspace_bytes(p, plan.nsplit);
+  if (workspace_bytes < need)
+    return fail(STREAMKL_ERROR_INVALID_VALUE,
+                std::string(what) + ": workspace too small (" + std::to_string(workspace_bytes) +
+                    " < " + std::to_string(need) + " bytes)");
+  const int64_t n = p->batch * p->heads * p->n_q;
+  const Span outs[4] = {flat_span(kl, n, 4), flat_span(lse1, n, 4), flat_span(lse2, n, 4),
+                        flat_span(workspace, (int64_t)need, 1)};
+  st = check_outputs(p, q1, k1, q2, k2, outs, 4, what);
+  if (st != STREAMKL_SUCCESS) return st;
+  if (split_blocks(s, plan) >= (1LL << 31))
+    return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": grid too large");
+  (void)hipGetLastError();
+  const bool sk = k1 == k2, causal = p->causal != 0;
+  float* part = static_cast<float*>(workspace);
+#define SKL_FWDS(DD, C, S) \
+  launch_fwd_split<DD, C, S>(s, plan, q1, k1, q2, k2, part, kl, lse1, lse2, stream)
+  if (p->head_dim == 64) {
+    if (causal) { if (sk) SKL_FWDS(64, true, true); else SKL_FWDS(64, true, false); }
+    else { if (sk) SKL_FWDS(64, false, true); else SKL_FWDS(64, false, false); }
+  } else {
+    if (causal) { if (sk) SKL_FWDS(128, true, true); else SKL_FWDS(128, true, false); }
+    else { if (sk) SKL_FWDS(128, false, true); else SKL_FWDS(128, false, false); }
+  }
+#undef SKL_FWDS
+  return check_launch(what);
+}
+
+streamkl_status_t fwd_one_pass(const streamkl_problem_t* p, const void* q1, const void* k1,
+                               const void* q2, const void* k2, float* kl, float* lse1,
+                               float* lse2, hipStream_t stream, const char* what) {
+  Shape s;
+  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
+  if (st != STREAMKL_SUCCESS) return st;
+  const int64_t n = p->batch * p->heads * p->n_q;
+  const Span outs[3] = {flat_span(kl, n, 4), flat_span(lse1, n, 4), flat_span(lse2, n, 4)};
+  st = check_outputs(p, q1, k1, q2, k2, outs, 3, what);
+  if (st != STREAMKL_SUCCESS) return st;
+  (void)hipGetLastError();
+  dispatch_fwd<Bf16In>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, kl, lse1, lse2,
+                       1.f, 1.f, stream);
   return check_launch(what);
 }
 
@@ -1881,20 +1987,31 @@ streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const voi
 
 extern "C" {
 
+size_t streamkl_fwd_workspace_size(const streamkl_problem_t* p) {
+  if (!sizes_ok(p)) return 0;
+  return fwd_auto_workspace(p);
+}
+
 streamkl_status_t streamkl_fwd(const streamkl_problem_t* p, const void* q1, const void* k1,
                                const void* q2, const void* k2, float* kl, float* lse1,
-                               float* lse2, hipStream_t stream) {
-  Shape s;
-  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
-  if (st != STREAMKL_SUCCESS) return st;
-  const int64_t n = p->batch * p->heads * p->n_q;
-  const Span outs[3] = {flat_span(kl, n, 4), flat_span(lse1, n, 4), flat_span(lse2, n, 4)};
-  st = check_outputs(p, q1, k1, q2, k2, outs, 3, "streamkl_fwd");
-  if (st != STREAMKL_SUCCESS) return st;
-  (void)hipGetLastError();
-  dispatch_fwd<Bf16In>(p->head_dim, p->causal != 0, k1 == k2, s, q1, k1, q2, k2, kl, lse1, lse2,
-                       1.f, 1.f, stream);
-  return check_launch("streamkl_fwd");
+                               float* lse2, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (!sizes_ok(p)) {
+    Shape s;
+    return validate(p, q1, k1, q2, k2, &s);
+  }
+  const SplitPlan plan = split_plan(p, 0);
+  if (plan.nsplit > 1)
+    return fwd_splitk_common(p, q1, k1, q2, k2, kl, lse1, lse2, plan, workspace, workspace_bytes,
+                             stream, "streamkl_fwd");
+  return fwd_one_pass(p, q1, k1, q2, k2, kl, lse1, lse2, stream, "streamkl_fwd");
+}
+
+streamkl_status_t streamkl_fwd_one_pass(const streamkl_problem_t* p, const void* q1,
+                                        const void* k1, const void* q2, const void* k2,
+                                        float* kl, float* lse1, float* lse2,
+                                        hipStream_t stream) {
+  return fwd_one_pass(p, q1, k1, q2, k2, kl, lse1, lse2, stream, "streamkl_fwd_one_pass");
 }
 
 streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* p, float descale1, float descale2,
@@ -1931,54 +2048,35 @@ streamkl_status_t streamkl_fwd_splitk(const streamkl_problem_t* p, const void* q
                                       float* lse1, float* lse2, int32_t n_splits,
                                       void* workspace, size_t workspace_bytes,
                                       hipStream_t stream) {
-  Shape s;
-  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
-  if (st != STREAMKL_SUCCESS) return st;
-  const SplitPlan plan = split_plan(p, n_splits);
-  const size_t need = split_workspace_bytes(p, plan.nsplit);
-  if (workspace_bytes < need)
-    return fail(STREAMKL_ERROR_INVALID_VALUE,
-                "streamkl_fwd_splitk: workspace too small (" + std::to_string(workspace_bytes) +
-                    " < " + std::to_string(need) + " bytes)");
-  const int64_t n = p->batch * p->heads * p->n_q;
-  const Span outs[4] = {flat_span(kl, n, 4), flat_span(lse1, n, 4), flat_span(lse2, n, 4),
-                        {reinterpret_cast<uintptr_t>(workspace),
-                         reinterpret_cast<uintptr_t>(workspace) + need}};
-  st = check_outputs(p, q1, k1, q2, k2, outs, 4, "streamkl_fwd_splitk");
-  if (st != STREAMKL_SUCCESS) return st;
-  if (split_blocks(s, plan) >= (1LL << 31))
-    return fail(STREAMKL_ERROR_INVALID_VALUE, "streamkl_fwd_splitk: grid too large");
-  (void)hipGetLastError();
-  const bool sk = k1 == k2, causal = p->causal != 0;
-  float* part = static_cast<float*>(workspace);
-#define SKL_FWDS(DD, C, S) \
-  launch_fwd_split<DD, C, S>(s, plan, q1, k1, q2, k2, part, kl, lse1, lse2, stream)
-  if (p->head_dim == 64) {
-    if (causal) { if (sk) SKL_FWDS(64, true, true); else SKL_FWDS(64, true, false); }
-    else { if (sk) SKL_FWDS(64, false, true); else SKL_FWDS(64, false, false); }
-  } else {
-    if (causal) { if (sk) SKL_FWDS(128, true, true); else SKL_FWDS(128, true, false); }
-    else { if (sk) SKL_FWDS(128, false, true); else SKL_FWDS(128, false, false); }
+  if (!sizes_ok(p)) {
+    Shape s;
+    return validate(p, q1, k1, q2, k2, &s);
   }
-#undef SKL_FWDS
-  return check_launch("streamkl_fwd_splitk");
+  return fwd_splitk_common(p, q1, k1, q2, k2, kl, lse1, lse2, split_plan(p, n_splits), workspace,
+                           workspace_bytes, stream, "streamkl_fwd_splitk");
+}
+
+size_t streamkl_bwd_workspace_size(const streamkl_problem_t* p) {
+  if (!sizes_ok(p) || (p->head_dim != 64 && p->head_dim != 128)) return 0;
+  return bwd_auto_plan(p).workspace;
 }
 
 streamkl_status_t streamkl_bwd_fixP1(const streamkl_problem_t* p, const void* q1,
                                      const void* k1, const void* q2, const void* k2,
                                      const float* lse1, const float* lse2, const float* grad_kl,
-                                     void* dq2, void* dk2, hipStream_t stream) {
+                                     void* dq2, void* dk2, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
   return bwd_common(p, 1, q1, k1, q2, k2, lse1, lse2, nullptr, grad_kl, dq2, dk2, true, true,
-                    stream, "streamkl_bwd_fixP1");
+                    stream, "streamkl_bwd_fixP1", BwdMode::kAuto, 0, workspace, workspace_bytes);
 }
 
 streamkl_status_t streamkl_bwd_fixP2(const streamkl_problem_t* p, const void* q1,
                                      const void* k1, const void* q2, const void* k2,
                                      const float* lse1, const float* lse2, const float* kl,
-                                     const float* grad_kl, void* dq1, void* dk1,
-                                     hipStream_t stream) {
+                                     const float* grad_kl, void* dq1, void* dk1, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
   return bwd_common(p, 2, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, dq1, dk1, true, true, stream,
-                    "streamkl_bwd_fixP2");
+                    "streamkl_bwd_fixP2", BwdMode::kAuto, 0, workspace, workspace_bytes);
 }
 
 streamkl_status_t streamkl_bwd_dq(const streamkl_problem_t* p, int32_t setting, const void* q1,
@@ -1986,7 +2084,7 @@ streamkl_status_t streamkl_bwd_dq(const streamkl_problem_t* p, int32_t setting, 
                                   const float* lse1, const float* lse2, const float* kl,
                                   const float* grad_kl, void* dq, hipStream_t stream) {
   return bwd_common(p, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, dq, nullptr, true, false,
-                    stream, "streamkl_bwd_dq");
+                    stream, "streamkl_bwd_dq", BwdMode::kOneKernel);
 }
 
 streamkl_status_t streamkl_bwd_dk(const streamkl_problem_t* p, int32_t setting, const void* q1,
@@ -1994,7 +2092,7 @@ streamkl_status_t streamkl_bwd_dk(const streamkl_problem_t* p, int32_t setting, 
                                   const float* lse1, const float* lse2, const float* kl,
                                   const float* grad_kl, void* dk, hipStream_t stream) {
   return bwd_common(p, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, nullptr, dk, false, true,
-                    stream, "streamkl_bwd_dk");
+                    stream, "streamkl_bwd_dk", BwdMode::kOneKernel);
 }
 
 int32_t streamkl_bwd_dq_splitk_default_splits(const streamkl_problem_t* p) {
@@ -2014,7 +2112,8 @@ streamkl_status_t streamkl_bwd_dq_splitk(const streamkl_problem_t* p, int32_t se
                                          int32_t n_splits, void* workspace,
                                          size_t workspace_bytes, hipStream_t stream) {
   return bwd_common(p, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, dq, nullptr, true, false,
-                    stream, "streamkl_bwd_dq_splitk", &n_splits, workspace, workspace_bytes);
+                    stream, "streamkl_bwd_dq_splitk", BwdMode::kSplitDq, n_splits, workspace,
+                    workspace_bytes);
 }
 
 size_t streamkl_bwd_fused_workspace_size(const streamkl_problem_t* p) {
@@ -2030,7 +2129,8 @@ streamkl_status_t streamkl_bwd_fused(const streamkl_problem_t* p, int32_t settin
                                      const float* grad_kl, void* dq, void* dk, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream) {
   return bwd_common(p, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, dq, dk, true, true,
-                    stream, "streamkl_bwd_fused", nullptr, workspace, workspace_bytes, true);
+                    stream, "streamkl_bwd_fused", BwdMode::kFused, 0, workspace,
+                    workspace_bytes);
 }
 
 const char* streamkl_status_string(streamkl_status_t status) {

@@ -53,9 +53,9 @@ Q1, K1, Q2, K2 = 0x10000000, 0x20000000, 0x30000000, 0x40000000
 O1, O2, O3 = 0x50000000, 0x60000000, 0x70000000
 
 
-def fwd(p, q1=Q1, k1=K1, q2=Q2, k2=K2, o=(O1, O2, O3)):
+def fwd(p, q1=Q1, k1=K1, q2=Q2, k2=K2, o=(O1, O2, O3), ws=None, nbytes=0):
     return skl.lib().streamkl_fwd(ctypes.byref(p) if p is not None else None, q1, k1, q2, k2,
-                                  *o, None)
+                                  *o, ws, nbytes, None)
 
 
 def last_error():
@@ -107,10 +107,12 @@ def test_invalid_pointers():
     assert fwd(p, o=(O1, O1 + 16, O3)) == 1
     L = skl.lib()
     # backward: outputs overlapping the lse / grad vectors are rejected
-    r = L.streamkl_bwd_fixP1(ctypes.byref(p), Q1, K1, Q2, K2, O1, O2, O3, O1, 0x7F000000, None)
+    WS = 0x7A000000
+    r = L.streamkl_bwd_fixP1(ctypes.byref(p), Q1, K1, Q2, K2, O1, O2, O3, O1, 0x7F000000, WS,
+                             1 << 30, None)
     assert r == 1
     r = L.streamkl_bwd_fixP2(ctypes.byref(p), Q1, K1, Q2, K2, O1, O2, None, O3, 0x7E000000,
-                             0x7F000000, None)
+                             0x7F000000, WS, 1 << 30, None)
     assert r == 1
 
 
@@ -238,3 +240,81 @@ def test_fused_workspace_and_limits():
     r = L.streamkl_bwd_fused(ctypes.byref(p), 2, Q1, K1, Q2, K2, O1, O2, None, 0x7C000000,
                              0x7D000000, 0x7E000000, WS, need, None)
     assert r == 1
+
+
+def test_adaptive_workspace_sizes_follow_the_plans():
+    """streamkl_fwd / streamkl_bwd_fixP1 / _fixP2 choose their kernels from the sizes; the
+    workspace they need is the chosen path's: split-K forward while its default plan has more
+    than one range, else none; fused backward for n_q <= 64, key-split dQ while its default plan
+    has more than one range, else none."""
+    L = skl.lib()
+    assert L.streamkl_fwd_workspace_size(None) == 0
+    assert L.streamkl_bwd_workspace_size(None) == 0
+    cases = ((1, 65536, 128, 32, 0), (16, 4096, 64, 2, 1), (64, 80, 128, 2, 0),
+             (65, 65536, 128, 32, 0), (512, 65536, 128, 32, 1), (4096, 4096, 128, 32, 0),
+             (65536, 65536, 128, 32, 1), (2048, 32768, 64, 128, 0), (300, 33, 64, 1, 1))
+    for nq, nk, d, heads, causal in cases:
+        p = good_problem(d)
+        p.n_q, p.n_k, p.heads, p.causal = nq, nk, heads, causal
+        ns = L.streamkl_fwd_splitk_default_splits(ctypes.byref(p))
+        fws = L.streamkl_fwd_workspace_size(ctypes.byref(p))
+        assert fws == (L.streamkl_fwd_splitk_workspace_size(ctypes.byref(p), 0) if ns > 1 else 0)
+        bws = L.streamkl_bwd_workspace_size(ctypes.byref(p))
+        if nq <= 64:
+            assert bws == L.streamkl_bwd_fused_workspace_size(ctypes.byref(p)) > 0
+        else:
+            assert bws == L.streamkl_bwd_dq_splitk_workspace_size(ctypes.byref(p), 0)
+    # the headline shape (32 heads x 64K rows) needs no workspace at all
+    p = good_problem()
+    p.n_q = p.n_k = 65536
+    p.heads, p.causal = 32, 1
+    assert L.streamkl_fwd_workspace_size(ctypes.byref(p)) == 0
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(p)) == 0
+    p.head_dim = 96
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(p)) == 0
+
+
+def test_adaptive_entry_points_check_the_workspace():
+    L = skl.lib()
+    WS = 0x7A000000
+    p = good_problem()
+    p.n_q, p.n_k, p.heads = 1, 65536, 32
+    for i, s in enumerate((32 * 65536 * 128, 65536 * 128, 128)):
+        p.k_stride[i] = s
+    for i, s in enumerate((32 * 128, 128, 128)):
+        p.q_stride[i] = s
+    # keys span 512 MiB from K1 and K2: put the outputs and the workspace past them
+    q1, q2, k1, k2 = 0x1000000000, 0x1100000000, 0x1200000000, 0x1300000000
+    o = (0x1400000000, 0x1400010000, 0x1400020000)
+    need = L.streamkl_fwd_workspace_size(ctypes.byref(p))
+    assert need > 0
+    ws = 0x1500000000
+
+    def f(ws, nbytes):
+        return L.streamkl_fwd(ctypes.byref(p), q1, k1, q2, k2, *o, ws, nbytes, None)
+    assert f(None, 0) == 1 and "workspace too small" in last_error()
+    assert f(ws, need - 4) == 1 and "workspace too small" in last_error()
+    assert f(ws + 8, need) == 1 and "aligned" in last_error()
+    assert f(k1 + 64, need) == 1 and "overlap" in last_error()
+    assert f(o[1], need) == 1 and "overlap" in last_error()
+    bneed = L.streamkl_bwd_workspace_size(ctypes.byref(p))
+    assert bneed > 0
+    g = 0x1400030000
+    dq, dk = 0x1600000000, 0x1700000000
+
+    def b1(ws, nbytes):
+        return L.streamkl_bwd_fixP1(ctypes.byref(p), q1, k1, q2, k2, o[1], o[2], g, dq, dk, ws,
+                                    nbytes, None)
+
+    def b2(ws, nbytes, kl=o[0]):
+        return L.streamkl_bwd_fixP2(ctypes.byref(p), q1, k1, q2, k2, o[1], o[2], kl, g, dq, dk,
+                                    ws, nbytes, None)
+    assert b1(None, 0) == 1 and "workspace too small" in last_error()
+    assert b1(ws, bneed - 1) == 1 and "workspace too small" in last_error()
+    assert b1(ws + 4, bneed) == 1 and "aligned" in last_error()
+    assert b1(dk + 64, bneed) == 1 and "overlap" in last_error()
+    assert b2(ws, bneed, kl=None) == 1
+    assert b2(None, 0) == 1 and "workspace too small" in last_error()
+    # one-pass forward: never a workspace; its own validation still applies
+    assert L.streamkl_fwd_one_pass(ctypes.byref(p), q1, k1, q2, k2, o[0], o[0], o[2], None) == 1
+    assert "overlap" in last_error()

@@ -41,12 +41,11 @@ def test_fused_matches_oracle_and_separate(shape, recipe):
         rdq, rdk = oracle.backward(setting, r["q1"], r["k1"], r["q2"], r["k2"], r["g"], w.scale,
                                    w.causal)
         check_grads(w, r, setting, dq, dk, rdq, rdk, lmax, tag="fused ")
-        if setting == 1:
-            sq, sk = skl.streamkl_bwd_fixP1(d["q1"], d["k1"], d["q2"], d["k2"], l1, l2, d["g"],
-                                            causal=w.causal)
-        else:
-            sq, sk = skl.streamkl_bwd_fixP2(d["q1"], d["k1"], d["q2"], d["k2"], l1, l2, kl,
-                                            d["g"], causal=w.causal)
+        # the one-kernel dQ and dK passes (what the adaptive entry points run at large n_q)
+        sq = skl.streamkl_bwd_dq(setting, d["q1"], d["k1"], d["q2"], d["k2"], l1, l2, kl, d["g"],
+                                 causal=w.causal)
+        sk = skl.streamkl_bwd_dk(setting, d["q1"], d["k1"], d["q2"], d["k2"], l1, l2, kl, d["g"],
+                                 causal=w.causal)
         # the same dS in float32 on both paths, other summation order, both rounded to bf16;
         # the float32 floor of the oracle comparison covers rows whose gradient is rounding
         # noise (e.g. a causal row that sees one key)

@@ -312,3 +312,40 @@ def test_signed_upstream_gradient(shape):
         # rows of opposite sign cancel in dK: the bf16 rounding of dS bounds that error
         check_grads(w, r, setting, dq, dk, rdq, rdk, lmax,
                     extra=bf16_ds_bound(setting, r, w.scale, w.causal))
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 300, 500, 128, False), (1, 2, 300, 300, 64, True),
+                                   (1, 2, 40, 700, 128, False)], ids=shape_id)
+def test_nan_input_row_leaves_other_rows_unaffected(shape):
+    """Non-finite inputs: the outputs that depend on them are unspecified, the others are not
+    affected. A NaN in one element of query row i of q1 (slice 1) may change KL, LSE and the dQ
+    row of that query only: every other query row's KL, LSE1, LSE2 and dQ (both settings) still
+    match the oracle on the clean inputs, and the other slice's dK too."""
+    announce(f"nan row {shape_id(shape)}")
+    w, d, r = make(shape, "perturb")
+    i = shape[2] // 2
+    q1 = d["q1"].clone()
+    q1[0, 1, i, 5] = float("nan")
+    kl, l1, l2 = skl.streamkl_fwd(q1, d["k1"], d["q2"], d["k2"], causal=w.causal)
+    rk, r1, r2 = oracle.forward(r["q1"], r["k1"], r["q2"], r["k2"], w.scale, w.causal)
+    keep = np.ones(shape[:3], dtype=bool)
+    keep[0, 1, i] = False
+    assert_rows_close(to_np(kl)[keep], rk[keep], "KL (other rows)")
+    assert_rows_close(to_np(l1)[keep], r1[keep], "LSE1 (other rows)")
+    assert_rows_close(to_np(l2)[keep], r2[keep], "LSE2 (other rows)")
+    lmax = max(np.abs(r1).max(), np.abs(r2).max())
+    for setting in (1, 2):
+        if setting == 1:
+            dq, dk = skl.streamkl_bwd_fixP1(q1, d["k1"], d["q2"], d["k2"], l1, l2, d["g"],
+                                            causal=w.causal)
+        else:
+            dq, dk = skl.streamkl_bwd_fixP2(q1, d["k1"], d["q2"], d["k2"], l1, l2, kl, d["g"],
+                                            causal=w.causal)
+        rdq, rdk = oracle.backward(setting, r["q1"], r["k1"], r["q2"], r["k2"], r["g"], w.scale,
+                                   w.causal)
+        qf, kf = (r["q2"], r["k2"]) if setting == 1 else (r["q1"], r["k1"])
+        aq = grad_atol(w.scale, r["g"], lmax, kf)
+        ak = grad_atol(w.scale, r["g"], lmax, qf, mass=w.n_q / w.n_k)
+        assert_grad_close(to_np(dq)[keep], rdq[keep], f"setting {setting} dQ (other rows)", aq)
+        # dK of slice 0 (slice 1's dK sums the NaN row and is unspecified)
+        assert_grad_close(to_np(dk)[0, 0], rdk[0, 0], f"setting {setting} dK (clean slice)", ak)

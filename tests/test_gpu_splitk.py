@@ -51,7 +51,7 @@ def test_splitk_matches_oracle(shape, recipe):
     print(f"splitk {shape_id(shape)} {recipe}", flush=True)
     w, d, r = make(shape, recipe)
     rk, r1, r2 = oracle.forward(r["q1"], r["k1"], r["q2"], r["k2"], w.scale, w.causal)
-    base = skl.streamkl_fwd(d["q1"], d["k1"], d["q2"], d["k2"], causal=w.causal)
+    base = skl.streamkl_fwd_one_pass(d["q1"], d["k1"], d["q2"], d["k2"], causal=w.causal)
     for n_splits in (0, 1, 3, 64, 65, 1000):
         kl, l1, l2 = skl.streamkl_fwd_splitk(d["q1"], d["k1"], d["q2"], d["k2"], causal=w.causal,
                                              n_splits=n_splits)
@@ -124,7 +124,7 @@ def test_splitk_blocks_at_64k_keys():
     dv = {n: dev_bf16(x[n]) for n in ("q1", "k1", "q2", "k2")}
     assert skl.streamkl_fwd_splitk_default_splits(dv["q1"], dv["k1"]) > 1
     kl, l1, l2 = skl.streamkl_fwd_splitk(dv["q1"], dv["k1"], dv["q2"], dv["k2"])
-    base = skl.streamkl_fwd(dv["q1"], dv["k1"], dv["q2"], dv["k2"])
+    base = skl.streamkl_fwd_one_pass(dv["q1"], dv["k1"], dv["q2"], dv["k2"])
     for a, b, what in zip((kl, l1, l2), base, ("KL", "LSE1", "LSE2")):
         assert_rows_close(to_np(a), to_np(b), what + " vs one-pass")
     rng = np.random.default_rng(3)

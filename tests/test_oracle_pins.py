@@ -248,3 +248,29 @@ def test_slice_independence():
             e = backward_slice(2, q1[b, h], k1[b, h], q2[b, h], k2[b, h], g[b, h], 0.3, True)
             np.testing.assert_array_equal(dq[b, h], e[0])
             np.testing.assert_array_equal(dk[b, h], e[1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dk_rows_slice_with_a_row_range_matches_the_all_rows_backward(causal):
+    """dk_rows_slice, the column-by-column dK that checks sampled keys at full sizes, against
+    the row-block backward over all rows: with rows = r0 .. n_q - 1 (causal) it must give the
+    complete dK of every key >= r0 (no row before r0 sees such a key), and with every row
+    (non-causal) the complete dK of any key; both settings."""
+    from oracle.reference import backward_slice, dk_rows_slice
+    rng = np.random.default_rng(21)
+    nq, nk, d = 90, 90, 16
+    q1, k1, q2, k2 = (rng.standard_normal((n, d)) for n in (nq, nk, nq, nk))
+    g = rng.uniform(0.2, 1.0, nq)
+    scale = d ** -0.5
+    r0 = 57 if causal else 0
+    keys = np.arange(r0, nk)[::3]
+    rows = np.arange(r0, nq)
+    for setting in (1, 2):
+        _, dk = backward_slice(setting, q1, k1, q2, k2, g, scale, causal)
+        got = dk_rows_slice(setting, q1, k1, q2, k2, g, scale, causal, keys, rows=rows)
+        np.testing.assert_allclose(got, dk[keys], rtol=1e-10, atol=1e-13)
+    if causal:
+        # a key before r0 is also seen by rows < r0: the truncated sum must differ there
+        _, dk = backward_slice(1, q1, k1, q2, k2, g, scale, causal)
+        early = dk_rows_slice(1, q1, k1, q2, k2, g, scale, causal, np.array([3]), rows=rows)
+        assert np.abs(early - dk[[3]]).max() > 1e-6

@@ -113,6 +113,27 @@ streamkl_status_t streamkl_fwd_one_pass(const streamkl_problem_t* problem, const
                                         float* kl, float* lse1, float* lse2, hipStream_t stream);
 
 /*
+ * Allocation-free forward, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same computation,
+ * kernel choice and outputs as streamkl_fwd, but when the split-K path needs a workspace it
+ * uses a scratch array that the library holds in device memory (one copy per GPU, kept until
+ * the process ends) instead of a caller buffer. The call allocates nothing and frees nothing.
+ * Limit: the split-K partial states must fit in streamkl_fwd_noalloc_max_workspace() bytes
+ * (4 MiB). The default plan never needs more than 3.75 MiB (at most 256 work items unsplit, cut
+ * into about 512 block items of 256 query rows or 4096 wavefront items of 32 rows, 5 floats per
+ * row and key range), so every size runs; a plan beyond the scratch would return
+ * STREAMKL_ERROR_NOT_SUPPORTED and enqueue nothing. The one-pass path needs no scratch.
+ * Every call on a GPU shares that GPU's scratch: calls that may overlap on one GPU (several
+ * streams, several host threads) race on it and must be ordered by the caller. The scratch is
+ * fully written before it is read within a call, so no clearing is needed between calls. The
+ * current HIP device must be the device of the buffers and of `stream`.
+ */
+size_t streamkl_fwd_noalloc_max_workspace(void);
+streamkl_status_t streamkl_fwd_noalloc(const streamkl_problem_t* problem, const void* q1,
+                                       const void* k1, const void* q2, const void* k2,
+                                       float* kl, float* lse1, float* lse2, hipStream_t stream);
+
+/*
  * Forward pass with OCP fp8 e4m3 inputs (mixed precision for the two Q K^T contractions,
  * float32 state; mixed precision is named as future work in the agents-report article's
  * conclusion). Same outputs and semantics as streamkl_fwd, with

@@ -9,6 +9,7 @@ Functions (names follow the C ABI):
   streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False)           -> (kl, lse1, lse2); adaptive
   streamkl_fwd_workspace_size(q1, k1, ...), streamkl_bwd_workspace_size(q1, k1, ...)
   streamkl_fwd_one_pass(q1, k1, q2, k2, ...)                        -> (kl, lse1, lse2)
+  streamkl_fwd_noalloc(q1, k1, q2, k2, ...)      -> (kl, lse1, lse2), library scratch, no allocation
   streamkl_fwd_fp8(q1, k1, q2, k2, descale1=1, descale2=1, ...)   -> (kl, lse1, lse2), fp8 inputs
   streamkl_fwd_splitk(q1, k1, q2, k2, n_splits=0, ...)             -> (kl, lse1, lse2)
   streamkl_fwd_splitk_default_splits(q1, k1, ...), streamkl_fwd_splitk_workspace_size(...)
@@ -35,6 +36,7 @@ STATUS = {0: "STREAMKL_SUCCESS", 1: "STREAMKL_ERROR_INVALID_VALUE",
           2: "STREAMKL_ERROR_NOT_SUPPORTED", 3: "STREAMKL_ERROR_HIP"}
 
 EXPORTS = ("streamkl_fwd", "streamkl_fwd_workspace_size", "streamkl_fwd_one_pass",
+           "streamkl_fwd_noalloc", "streamkl_fwd_noalloc_max_workspace",
            "streamkl_fwd_fp8", "streamkl_fwd_splitk", "streamkl_fwd_splitk_default_splits",
            "streamkl_fwd_splitk_workspace_size", "streamkl_bwd_workspace_size",
            "streamkl_bwd_fixP1", "streamkl_bwd_fixP2",
@@ -79,6 +81,10 @@ def lib(path: str | None = None) -> ctypes.CDLL:
     L.streamkl_fwd_one_pass.restype = ctypes.c_int
     L.streamkl_bwd_workspace_size.argtypes = [pp]
     L.streamkl_bwd_workspace_size.restype = ctypes.c_size_t
+    L.streamkl_fwd_noalloc.argtypes = [pp, vp, vp, vp, vp, fp, fp, fp, vp]
+    L.streamkl_fwd_noalloc.restype = ctypes.c_int
+    L.streamkl_fwd_noalloc_max_workspace.argtypes = []
+    L.streamkl_fwd_noalloc_max_workspace.restype = ctypes.c_size_t
     L.streamkl_fwd_fp8.argtypes = [pp, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, fp, fp, fp,
                                    vp]
     L.streamkl_fwd_fp8.restype = ctypes.c_int
@@ -202,6 +208,18 @@ def streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False, out=None, workspace=N
     _check(lib().streamkl_fwd(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
                               k2.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
                               out[2].data_ptr(), wp, wn, _stream(q1)))
+    return out
+
+
+def streamkl_fwd_noalloc(q1, k1, q2, k2, scale=None, causal=False, out=None):
+    """streamkl_fwd with any split-K workspace taken from the library's static device scratch
+    (no allocation by the library; `out` may be given to allocate nothing here either)."""
+    _check_inputs(q1, k1, q2, k2)
+    out = _fwd_out(q1, out)
+    p = make_problem(q1, k1, scale, causal)
+    _check(lib().streamkl_fwd_noalloc(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(),
+                                      q2.data_ptr(), k2.data_ptr(), out[0].data_ptr(),
+                                      out[1].data_ptr(), out[2].data_ptr(), _stream(q1)))
     return out
 
 

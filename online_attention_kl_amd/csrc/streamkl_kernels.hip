@@ -50,6 +50,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -1983,6 +1984,41 @@ streamkl_status_t fwd_one_pass(const streamkl_problem_t* p, const void* q1, cons
   return check_launch(what);
 }
 
+// ---------------------------------------------------------------- static scratch
+// Device memory of the allocation-free forward (streamkl_fwd_noalloc): the split-K partial
+// states live in this file-scope array instead of a caller workspace. Each GPU the library runs
+// on holds its own copy until the process ends. In host code `scratch` names a host-side
+// stand-in, not a device address: the device address of each GPU's copy is looked up once per
+// device with hipGetSymbolAddress (with that device current) and only that address is used.
+// The forward's default plan never needs more than 3.75 MiB of partial states: at most 256 work
+// items unsplit, split into at most about 512 block items (256-row query blocks) or 4096
+// wavefront items (32-row blocks), 5 floats per row and range, i.e. < 256 * 768 * 20 bytes.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's scratch copy (looked up on the first call per device).
+streamkl_status_t scratch_address(void** out, const char* what) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(STREAMKL_ERROR_HIP, std::string(what) + ": hipGetDevice: " + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(STREAMKL_ERROR_NOT_SUPPORTED, std::string(what) + ": device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(STREAMKL_ERROR_HIP, std::string(what) + ": hipGetSymbolAddress: " + hipGetErrorString(e));
+    g_scratch_addr[dev] = ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return STREAMKL_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2012,6 +2048,40 @@ streamkl_status_t streamkl_fwd_one_pass(const streamkl_problem_t* p, const void*
                                         float* kl, float* lse1, float* lse2,
                                         hipStream_t stream) {
   return fwd_one_pass(p, q1, k1, q2, k2, kl, lse1, lse2, stream, "streamkl_fwd_one_pass");
+}
+
+size_t streamkl_fwd_noalloc_max_workspace(void) { return kScratchBytes; }
+
+streamkl_status_t streamkl_fwd_noalloc(const streamkl_problem_t* p, const void* q1,
+                                       const void* k1, const void* q2, const void* k2, float* kl,
+                                       float* lse1, float* lse2, hipStream_t stream) {
+  if (!sizes_ok(p)) {
+    Shape s;
+    return validate(p, q1, k1, q2, k2, &s);
+  }
+  const SplitPlan plan = split_plan(p, 0);
+  if (plan.nsplit <= 1)
+    return fwd_one_pass(p, q1, k1, q2, k2, kl, lse1, lse2, stream, "streamkl_fwd_noalloc");
+  const size_t need = split_workspace_bytes(p, plan.nsplit);
+  if (need > kScratchBytes)
+    return fail(STREAMKL_ERROR_NOT_SUPPORTED,
+                "streamkl_fwd_noalloc: the split-K partial states need " + std::to_string(need) +
+                    " bytes, more than the " + std::to_string(kScratchBytes) +
+                    " bytes of the library's scratch; use streamkl_fwd with a workspace");
+  // validation first (inputs, outputs, overlaps): an invalid call makes no device call at all,
+  // not even the scratch lookup
+  Shape s;
+  streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
+  if (st != STREAMKL_SUCCESS) return st;
+  const int64_t n = p->batch * p->heads * p->n_q;
+  const Span outs[3] = {flat_span(kl, n, 4), flat_span(lse1, n, 4), flat_span(lse2, n, 4)};
+  st = check_outputs(p, q1, k1, q2, k2, outs, 3, "streamkl_fwd_noalloc");
+  if (st != STREAMKL_SUCCESS) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws, "streamkl_fwd_noalloc");
+  if (st != STREAMKL_SUCCESS) return st;
+  return fwd_splitk_common(p, q1, k1, q2, k2, kl, lse1, lse2, plan, ws, kScratchBytes, stream,
+                           "streamkl_fwd_noalloc");
 }
 
 streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* p, float descale1, float descale2,

@@ -318,3 +318,29 @@ def test_adaptive_entry_points_check_the_workspace():
     # one-pass forward: never a workspace; its own validation still applies
     assert L.streamkl_fwd_one_pass(ctypes.byref(p), q1, k1, q2, k2, o[0], o[0], o[2], None) == 1
     assert "overlap" in last_error()
+
+
+def test_noalloc_forward_scratch_covers_every_plan_and_validates():
+    """streamkl_fwd_noalloc: the library's 4 MiB scratch holds the split-K partial states of the
+    default plan at every size (swept here), and invalid calls are refused before any device
+    call."""
+    L = skl.lib()
+    cap = L.streamkl_fwd_noalloc_max_workspace()
+    assert cap == 4 << 20
+    worst = 0
+    for bh in (1, 2, 3, 7, 8, 32, 100, 255, 256, 257, 1024):
+        for nq in (1, 16, 32, 33, 64, 200, 256, 257, 511, 4096):
+            for nk in (1, 100, 4096, 65536, 1 << 22):
+                for causal in (0, 1):
+                    p = good_problem()
+                    p.heads, p.n_q, p.n_k, p.causal = bh, nq, nk, causal
+                    worst = max(worst, L.streamkl_fwd_workspace_size(ctypes.byref(p)))
+    assert 3 << 20 < worst <= cap
+    assert L.streamkl_fwd_noalloc(None, Q1, K1, Q2, K2, O1, O2, O3, None) == 1
+    p = good_problem()
+    p.n_q, p.n_k = 1, 4096
+    assert 0 < L.streamkl_fwd_workspace_size(ctypes.byref(p)) <= cap
+    assert L.streamkl_fwd_noalloc(ctypes.byref(p), Q1, K1, Q2, K2, O1, O1, O3, None) == 1
+    assert "overlap" in last_error()
+    assert L.streamkl_fwd_noalloc(ctypes.byref(p), Q1, K1 + 8, Q2, K2, O1, O2, O3, None) == 1
+    assert "aligned" in last_error()

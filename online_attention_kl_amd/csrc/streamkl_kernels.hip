@@ -50,6 +50,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstring>
 #include <mutex>
 #include <string>
 #include <type_traits>
@@ -2204,13 +2205,18 @@ streamkl_status_t streamkl_bwd_fused(const streamkl_problem_t* p, int32_t settin
 }
 
 const char* streamkl_status_string(streamkl_status_t status) {
-  switch (status) {
+  // a C caller may pass any int: read the bytes, since loading an out-of-range value as the
+  // enum type is undefined in C++
+  int code;
+  static_assert(sizeof(code) == sizeof(status), "the status enum is int-sized");
+  std::memcpy(&code, &status, sizeof(code));
+  switch (code) {
     case STREAMKL_SUCCESS: return "STREAMKL_SUCCESS";
     case STREAMKL_ERROR_INVALID_VALUE: return "STREAMKL_ERROR_INVALID_VALUE";
     case STREAMKL_ERROR_NOT_SUPPORTED: return "STREAMKL_ERROR_NOT_SUPPORTED";
     case STREAMKL_ERROR_HIP: return "STREAMKL_ERROR_HIP";
+    default: return "STREAMKL_UNKNOWN_STATUS";
   }
-  return "STREAMKL_UNKNOWN_STATUS";
 }
 
 const char* streamkl_last_error(void) { return g_last_error.c_str(); }

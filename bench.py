@@ -165,6 +165,19 @@ def summarize_counters(dirs) -> str:
     return "\n".join(lines)
 
 
+def algorithmic_bytes(w) -> int:
+    """Bytes one step must move at least: the forward reads Q1, K1, Q2, K2 once (K once when
+    shared) and writes KL, LSE1, LSE2; each backward setting reads the four inputs, LSE1, LSE2,
+    g (and KL for setting 2) and writes dQ and dK in bf16."""
+    B, H, nq, nk, d = w.batch, w.heads, w.n_q, w.n_k, w.head_dim
+    qb, kb, row = B * H * nq * d * 2, B * H * nk * d * 2, B * H * nq * 4
+    kin = kb if w.shared_k else 2 * kb
+    total = 2 * qb + kin + 3 * row
+    for s_ in w.settings:
+        total += 2 * qb + kin + (3 if s_ == 1 else 4) * row + qb + kb
+    return total
+
+
 def cpu_model() -> str:
     """The host CPU's model name (first "model name" line of /proc/cpuinfo), or "unknown"."""
     try:
@@ -571,6 +584,16 @@ def configs_mode(args):
 
         pairs = visible_pairs(w)
         flop = (4 + 8 * len(w.settings)) * w.head_dim * pairs
+        nbytes = algorithmic_bytes(w)
+        ws = {"fwd": int(wsf.numel()) if skl.streamkl_fwd_workspace_size(
+                  q1, k1, causal=w.causal) else 0,
+              "bwd": int(wsb.numel()) if skl.streamkl_bwd_workspace_size(
+                  q1, k1, causal=w.causal) else 0}
+        oracle = None
+        if not args.no_cpu_baseline:
+            print(f"[bench] {w.name}: timing the fp64 oracle on a host sample", file=sys.stderr,
+                  flush=True)
+            oracle = cpu_baseline(w, x, args.cpu_seconds / 3)
         for flush in ((False, True) if name in ("tiny_256_d64", "nc_4k_d128") else (False,)):
             # at least --warmup steps and 0.3 s of them, so that short steps do not start timing
             # before the clocks have risen
@@ -597,7 +620,13 @@ def configs_mode(args):
                            "n_q": w.n_q, "n_k": w.n_k, "head_dim": w.head_dim,
                            "causal": w.causal, "backward_settings": list(w.settings)},
                 "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
-                "pct_bf16_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+                "pct_bf16_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                "algorithmic_bytes_per_step": nbytes,
+                "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "workspace_bytes": ws,
+                "cpu_baseline": oracle,
+                "gpu_vs_oracle": (round(tf / oracle["value"], 1) if oracle else None)}),
+                  flush=True)
         del q1, q2, k1, k2, g, kl, l1, l2, grads
         torch.cuda.empty_cache()
 

@@ -761,7 +761,9 @@ struct BwdStage {
 
   __device__ __forceinline__ bool mine(int i, int& te, int& row, int& chunk) const {
     const int gid = threadIdx.x + i * kBwdThreads;
-    te = gid / PER;
+    // when a tensor's chunks are a whole number of block-widths, chunk i of every thread belongs
+    // to tensor i * kBwdThreads / PER: known at compile time, so no per-lane branch on it
+    te = PER % kBwdThreads == 0 ? (i * kBwdThreads) / PER : gid / PER;
     const int rem = gid - te * PER;
     row = rem % kBT;
     chunk = rem / kBT;

@@ -29,6 +29,10 @@ SHAPES = [
     (1, 3, 384, 384, 128, False),
     # many slices: the block -> (slice, row block) mapping over 128 slices
     (8, 16, 70, 90, 64, True),
+    # a multiple of 8 slices with several row blocks each: every XCD runs whole slices, their
+    # row blocks in order (ragged last blocks on both sides)
+    (2, 4, 600, 520, 128, True),
+    (1, 8, 1000, 1000, 64, False),
 ]
 
 

@@ -1496,10 +1496,24 @@ struct Span {
 
 bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// Bytes from a [B, H, N, D] tensor's first element to one past its last, or -1 when that does
+// not fit in 62 bits (no memory has such strides).
+int64_t tensor_extent(int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* st,
+                      int64_t elem) {
+  int64_t a, b, c, sum;
+  if (__builtin_mul_overflow(B - 1, st[0], &a) || __builtin_mul_overflow(H - 1, st[1], &b) ||
+      __builtin_mul_overflow(N - 1, st[2], &c) || __builtin_add_overflow(a, b, &sum) ||
+      __builtin_add_overflow(sum, c, &sum) || __builtin_add_overflow(sum, D, &sum) ||
+      __builtin_mul_overflow(sum, elem, &sum) || sum >= ((int64_t)1 << 62))
+    return -1;
+  return sum;
+}
+
+// Byte range of a tensor whose extent validate() has accepted.
 Span tensor_span(const void* p, int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* st,
                  int64_t elem) {
-  const int64_t last = (B - 1) * st[0] + (H - 1) * st[1] + (N - 1) * st[2] + D;
-  return {reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (uintptr_t)(last * elem)};
+  const int64_t ext = tensor_extent(B, H, N, D, st, elem);
+  return {reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (uintptr_t)ext};
 }
 
 Span flat_span(const void* p, int64_t n, int64_t elem) {
@@ -1517,7 +1531,9 @@ streamkl_status_t validate(const streamkl_problem_t* p, const void* q1, const vo
     return fail(STREAMKL_ERROR_INVALID_VALUE, "scale must be finite and > 0");
   if (p->causal != 0 && p->causal != 1) return fail(STREAMKL_ERROR_INVALID_VALUE, "causal must be 0 or 1");
   const int64_t lim = (int64_t)1 << 30;
-  if (p->n_q >= lim || p->n_k >= lim || p->batch * p->heads >= lim)
+  // each factor is bounded before the product is formed (no signed overflow)
+  if (p->batch >= lim || p->heads >= lim || p->n_q >= lim || p->n_k >= lim ||
+      p->batch * p->heads >= lim)
     return fail(STREAMKL_ERROR_INVALID_VALUE, "sizes too large");
   const int64_t nblk = (p->n_q > p->n_k ? p->n_q : p->n_k) / 128 + 1;
   if (nblk * p->batch * p->heads >= ((int64_t)1 << 31))
@@ -1533,10 +1549,18 @@ streamkl_status_t validate(const streamkl_problem_t* p, const void* q1, const vo
   if (p->q_stride[2] * elem_bytes >= kMaxRowStrideBytes ||
       p->k_stride[2] * elem_bytes >= kMaxRowStrideBytes)
     return fail(STREAMKL_ERROR_NOT_SUPPORTED, "row strides must be below 16 MiB");
+  const int64_t qext = tensor_extent(p->batch, p->heads, p->n_q, p->head_dim, p->q_stride, elem_bytes);
+  const int64_t kext = tensor_extent(p->batch, p->heads, p->n_k, p->head_dim, p->k_stride, elem_bytes);
+  if (qext < 0 || kext < 0)
+    return fail(STREAMKL_ERROR_INVALID_VALUE, "strides too large: a tensor's extent overflows");
   const void* in[4] = {q1, k1, q2, k2};
-  for (const void* x : in) {
+  const int64_t ext[4] = {qext, kext, qext, kext};
+  for (int i = 0; i < 4; ++i) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(in[i]);
     if (!x) return fail(STREAMKL_ERROR_INVALID_VALUE, "input pointer is NULL");
-    if (reinterpret_cast<uintptr_t>(x) % 16) return fail(STREAMKL_ERROR_INVALID_VALUE, "inputs must be 16-byte aligned");
+    if (x % 16) return fail(STREAMKL_ERROR_INVALID_VALUE, "inputs must be 16-byte aligned");
+    if (x > UINTPTR_MAX - (uintptr_t)ext[i])
+      return fail(STREAMKL_ERROR_INVALID_VALUE, "an input's extent wraps the address space");
   }
   s->nq = (int)p->n_q;
   s->nk = (int)p->n_k;
@@ -1563,6 +1587,8 @@ streamkl_status_t check_outputs(const streamkl_problem_t* p, const void* q1, con
   for (int i = 0; i < n_out; ++i) {
     if (outs[i].lo == 0) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": output pointer is NULL");
     if (outs[i].lo % 16) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": outputs must be 16-byte aligned");
+    if (outs[i].hi < outs[i].lo)
+      return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": an output's extent wraps the address space");
     for (const Span& x : in)
       if (overlaps(outs[i], x)) return fail(STREAMKL_ERROR_INVALID_VALUE, std::string(what) + ": output overlaps an input");
     for (int j = 0; j < i; ++j)
@@ -1943,12 +1969,30 @@ streamkl_status_t bwd_common(const streamkl_problem_t* p, int setting, const voi
   return check_launch(what);
 }
 
-// The forward's adaptive choice: the split-K path when its plan cuts the keys into more than
-// one range (few query blocks for the chip), else the one-pass kernel with no workspace.
+// The size bounds that validate() enforces (every size at least 1 and below 2^30, batch x heads
+// below 2^30, a grid below 2^31 blocks), as a plain test. The plans are integer arithmetic on
+// the sizes and are computed before validate() runs (and the size queries never run it), so
+// every caller of a plan checks this first.
 bool sizes_ok(const streamkl_problem_t* p) {
-  return p && p->batch >= 1 && p->heads >= 1 && p->n_q >= 1 && p->n_k >= 1;
+  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1) return false;
+  const int64_t lim = (int64_t)1 << 30;
+  if (p->batch >= lim || p->heads >= lim || p->n_q >= lim || p->n_k >= lim ||
+      p->batch * p->heads >= lim)
+    return false;
+  const int64_t nblk = (p->n_q > p->n_k ? p->n_q : p->n_k) / 128 + 1;
+  return nblk * p->batch * p->heads < ((int64_t)1 << 31);
 }
 
+// The error of a call whose sizes fail sizes_ok(): validate()'s message.
+streamkl_status_t sizes_error(const streamkl_problem_t* p, const void* q1, const void* k1,
+                              const void* q2, const void* k2) {
+  Shape s;
+  const streamkl_status_t st = validate(p, q1, k1, q2, k2, &s);
+  return st != STREAMKL_SUCCESS ? st : fail(STREAMKL_ERROR_INVALID_VALUE, "sizes out of range");
+}
+
+// The forward's adaptive choice: the split-K path when its plan cuts the keys into more than
+// one range (few query blocks for the chip), else the one-pass kernel with no workspace.
 size_t fwd_auto_workspace(const streamkl_problem_t* p) {
   const SplitPlan plan = split_plan(p, 0);
   return plan.nsplit > 1 ? split_workspace_bytes(p, plan.nsplit) : 0;
@@ -2053,10 +2097,7 @@ streamkl_status_t streamkl_fwd(const streamkl_problem_t* p, const void* q1, cons
                                const void* q2, const void* k2, float* kl, float* lse1,
                                float* lse2, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
-  if (!sizes_ok(p)) {
-    Shape s;
-    return validate(p, q1, k1, q2, k2, &s);
-  }
+  if (!sizes_ok(p)) return sizes_error(p, q1, k1, q2, k2);
   const SplitPlan plan = split_plan(p, 0);
   if (plan.nsplit > 1)
     return fwd_splitk_common(p, q1, k1, q2, k2, kl, lse1, lse2, plan, workspace, workspace_bytes,
@@ -2076,10 +2117,7 @@ size_t streamkl_fwd_noalloc_max_workspace(void) { return kScratchBytes; }
 streamkl_status_t streamkl_fwd_noalloc(const streamkl_problem_t* p, const void* q1,
                                        const void* k1, const void* q2, const void* k2, float* kl,
                                        float* lse1, float* lse2, hipStream_t stream) {
-  if (!sizes_ok(p)) {
-    Shape s;
-    return validate(p, q1, k1, q2, k2, &s);
-  }
+  if (!sizes_ok(p)) return sizes_error(p, q1, k1, q2, k2);
   const SplitPlan plan = split_plan(p, 0);
   if (plan.nsplit <= 1)
     return fwd_one_pass(p, q1, k1, q2, k2, kl, lse1, lse2, stream, "streamkl_fwd_noalloc");
@@ -2125,12 +2163,12 @@ streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* p, float descale1, 
 }
 
 int32_t streamkl_fwd_splitk_default_splits(const streamkl_problem_t* p) {
-  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1) return 0;
+  if (!sizes_ok(p)) return 0;
   return split_plan(p, 0).nsplit;
 }
 
 size_t streamkl_fwd_splitk_workspace_size(const streamkl_problem_t* p, int32_t n_splits) {
-  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1) return 0;
+  if (!sizes_ok(p)) return 0;
   return split_workspace_bytes(p, split_plan(p, n_splits).nsplit);
 }
 
@@ -2139,10 +2177,7 @@ streamkl_status_t streamkl_fwd_splitk(const streamkl_problem_t* p, const void* q
                                       float* lse1, float* lse2, int32_t n_splits,
                                       void* workspace, size_t workspace_bytes,
                                       hipStream_t stream) {
-  if (!sizes_ok(p)) {
-    Shape s;
-    return validate(p, q1, k1, q2, k2, &s);
-  }
+  if (!sizes_ok(p)) return sizes_error(p, q1, k1, q2, k2);
   return fwd_splitk_common(p, q1, k1, q2, k2, kl, lse1, lse2, split_plan(p, n_splits), workspace,
                            workspace_bytes, stream, "streamkl_fwd_splitk");
 }
@@ -2187,12 +2222,12 @@ streamkl_status_t streamkl_bwd_dk(const streamkl_problem_t* p, int32_t setting, 
 }
 
 int32_t streamkl_bwd_dq_splitk_default_splits(const streamkl_problem_t* p) {
-  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1) return 0;
+  if (!sizes_ok(p)) return 0;
   return dq_split_plan(p, 0).nsplit;
 }
 
 size_t streamkl_bwd_dq_splitk_workspace_size(const streamkl_problem_t* p, int32_t n_splits) {
-  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1) return 0;
+  if (!sizes_ok(p)) return 0;
   return dq_split_workspace_bytes(p, dq_split_plan(p, n_splits).nsplit);
 }
 
@@ -2208,8 +2243,7 @@ streamkl_status_t streamkl_bwd_dq_splitk(const streamkl_problem_t* p, int32_t se
 }
 
 size_t streamkl_bwd_fused_workspace_size(const streamkl_problem_t* p) {
-  if (!p || p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_k < 1 || p->n_q > kFusedMaxQ ||
-      (p->head_dim != 64 && p->head_dim != 128))
+  if (!sizes_ok(p) || p->n_q > kFusedMaxQ || (p->head_dim != 64 && p->head_dim != 128))
     return 0;
   return fused_workspace_bytes(p);
 }

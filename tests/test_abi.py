@@ -98,6 +98,44 @@ def test_invalid_problem_values():
     assert fwd(p) == 1 and "overlap" in last_error()
 
 
+def test_sizes_and_strides_that_overflow():
+    # each of batch and heads is bounded before their product is formed
+    p = good_problem()
+    p.batch, p.heads = 1 << 40, 1 << 40
+    assert fwd(p) == 1 and "too large" in last_error()
+    # the size queries plan from the sizes: out-of-range sizes give 0, not a plan
+    L, pp = skl.lib(), ctypes.byref(p)
+    assert L.streamkl_fwd_workspace_size(pp) == 0
+    assert L.streamkl_bwd_workspace_size(pp) == 0
+    assert L.streamkl_fwd_splitk_default_splits(pp) == 0
+    assert L.streamkl_fwd_splitk_workspace_size(pp, 0) == 0
+    assert L.streamkl_bwd_dq_splitk_default_splits(pp) == 0
+    assert L.streamkl_bwd_dq_splitk_workspace_size(pp, 0) == 0
+    assert L.streamkl_bwd_fused_workspace_size(pp) == 0
+    q = good_problem()
+    # each size in range, the grid not: 1024 slices x (2^29 / 128 + 1) blocks >= 2^31
+    q.heads, q.n_q, q.n_k = 1024, 1 << 29, 1 << 29
+    assert L.streamkl_fwd_workspace_size(ctypes.byref(q)) == 0
+    assert fwd(q) == 1 and "grid" in last_error()
+    p = good_problem()
+    p.batch = 1 << 31
+    assert fwd(p) == 1 and "too large" in last_error()
+    # a batch stride whose extent does not fit in 62 bits
+    p = good_problem()
+    p.batch = 4
+    p.k_stride[0] = 1 << 61
+    assert fwd(p) == 1 and "extent" in last_error()
+    p = good_problem()
+    p.batch = 3
+    p.q_stride[0] = (1 << 63) - 8
+    assert fwd(p) == 1 and "extent" in last_error()
+    # an input whose extent would wrap past the top of the address space
+    p = good_problem()
+    assert fwd(p, k2=(1 << 64) - 4096) == 1 and "wraps" in last_error()
+    # an output that wraps
+    assert fwd(p, o=(O1, O2, (1 << 64) - 16)) == 1 and "wraps" in last_error()
+
+
 def test_invalid_pointers():
     p = good_problem()
     assert fwd(p, q1=0) == 1

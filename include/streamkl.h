@@ -16,6 +16,11 @@
  *    streamkl_problem_t (the head_dim axis is contiguous). All pointers must be 16-byte aligned
  *    and every stride a multiple of 8 elements. Row strides of 16 MiB or more are not supported
  *    (STREAMKL_ERROR_NOT_SUPPORTED): tiles are addressed with 32-bit offsets from a tile base.
+ *  - Size limits (STREAMKL_ERROR_INVALID_VALUE beyond them): batch, heads, n_q, n_k and
+ *    batch * heads below 2^30; batch * heads * (max(n_q, n_k) / 128 + 1) below 2^31 (grid
+ *    size); each tensor's extent (from its first element to one past its last, through the
+ *    strides) below 2^62 bytes and not wrapping past the top of the address space. The size
+ *    queries return 0 for problems outside these limits.
  *  - Causal masking is top-left: key j is visible to query i iff j <= i. Every row then has at
  *    least one visible key.
  *  - Logits are S_t = scale * Q_t K_t^T; LSE values use the natural logarithm.

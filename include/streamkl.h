@@ -26,7 +26,8 @@
  *  - Logits are S_t = scale * Q_t K_t^T; LSE values use the natural logarithm.
  *  - The caller owns every buffer. The library never allocates, frees or synchronises device
  *    memory; every call enqueues kernels on `stream` and returns without waiting. Buffers must
- *    stay valid until the stream has executed the work. There is no global mutable state apart
+ *    stay valid until the stream has executed the work, and live on the device of `stream`
+ *    (the current device for the null stream). There is no global mutable state apart
  *    from a thread-local error message, so calls from several host threads are safe.
  *  - Validation happens before anything is enqueued: an invalid call returns an error status
  *    and touches no buffer. A launch failure returns STREAMKL_ERROR_HIP; outputs are then
@@ -131,7 +132,8 @@ streamkl_status_t streamkl_fwd_one_pass(const streamkl_problem_t* problem, const
  * Every call on a GPU shares that GPU's scratch: calls that may overlap on one GPU (several
  * streams, several host threads) race on it and must be ordered by the caller. The scratch is
  * fully written before it is read within a call, so no clearing is needed between calls. The
- * current HIP device must be the device of the buffers and of `stream`.
+ * scratch copy used is the one on the device of `stream` (the current device for the null
+ * stream); its address is looked up on the first call for that device.
  */
 size_t streamkl_fwd_noalloc_max_workspace(void);
 streamkl_status_t streamkl_fwd_noalloc(const streamkl_problem_t* problem, const void* q1,

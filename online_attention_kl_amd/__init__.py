@@ -129,6 +129,21 @@ def _check(status: int):
         raise StreamKLError(status, msg)
 
 
+def _run(t, fn, *args):
+    """Calls a library entry point with t's device current, as the launch context of its
+    kernels, and raises on an error status."""
+    import torch
+    with torch.cuda.device(t.device):
+        status = fn(*args)
+    _check(status)
+
+
+def _same_device(dev, *named):
+    for name, t in named:
+        if t is not None and (not t.is_cuda or t.device != dev):
+            raise ValueError(f"{name} must be a CUDA tensor on {dev}, the device of q1")
+
+
 def make_problem(q1, k1, scale, causal) -> Problem:
     B, H, nq, d = q1.shape
     nk = k1.shape[2]
@@ -154,13 +169,15 @@ def _check_inputs(q1, k1, q2, k2):
         raise ValueError("k1 and k2 must have the same shape and strides")
     if k1.shape[:2] != q1.shape[:2] or k1.shape[3] != q1.shape[3]:
         raise ValueError("q and k must agree on batch, heads and head_dim")
+    _same_device(q1.device, ("k1", k1), ("q2", q2), ("k2", k2))
 
 
-def _rowvec(t, name, shape):
+def _rowvec(t, name, shape, dev):
     import torch
     if not t.is_cuda or t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) \
             or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape {shape}")
+    _same_device(dev, (name, t))
 
 
 def _stream(t):
@@ -178,6 +195,7 @@ def _workspace(need, workspace, device):
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous CUDA tensor")
+    _same_device(device, ("workspace", workspace))
     return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
 
 
@@ -188,7 +206,7 @@ def _fwd_out(q1, out):
         out = tuple(torch.empty((B, H, nq), dtype=torch.float32, device=q1.device)
                     for _ in range(3))
     for n, t in zip(("kl", "lse1", "lse2"), out):
-        _rowvec(t, n, (B, H, nq))
+        _rowvec(t, n, (B, H, nq), q1.device)
     return out
 
 
@@ -205,9 +223,9 @@ def streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False, out=None, workspace=N
     p = make_problem(q1, k1, scale, causal)
     need = int(lib().streamkl_fwd_workspace_size(ctypes.byref(p)))
     wp, wn, _keep = _workspace(need, workspace, q1.device)
-    _check(lib().streamkl_fwd(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
-                              k2.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
-                              out[2].data_ptr(), wp, wn, _stream(q1)))
+    _run(q1, lib().streamkl_fwd, ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
+         k2.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
+         out[2].data_ptr(), wp, wn, _stream(q1))
     return out
 
 
@@ -217,9 +235,9 @@ def streamkl_fwd_noalloc(q1, k1, q2, k2, scale=None, causal=False, out=None):
     _check_inputs(q1, k1, q2, k2)
     out = _fwd_out(q1, out)
     p = make_problem(q1, k1, scale, causal)
-    _check(lib().streamkl_fwd_noalloc(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(),
-                                      q2.data_ptr(), k2.data_ptr(), out[0].data_ptr(),
-                                      out[1].data_ptr(), out[2].data_ptr(), _stream(q1)))
+    _run(q1, lib().streamkl_fwd_noalloc, ctypes.byref(p), q1.data_ptr(), k1.data_ptr(),
+         q2.data_ptr(), k2.data_ptr(), out[0].data_ptr(),
+         out[1].data_ptr(), out[2].data_ptr(), _stream(q1))
     return out
 
 
@@ -228,9 +246,9 @@ def streamkl_fwd_one_pass(q1, k1, q2, k2, scale=None, causal=False, out=None):
     _check_inputs(q1, k1, q2, k2)
     out = _fwd_out(q1, out)
     p = make_problem(q1, k1, scale, causal)
-    _check(lib().streamkl_fwd_one_pass(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(),
-                                       q2.data_ptr(), k2.data_ptr(), out[0].data_ptr(),
-                                       out[1].data_ptr(), out[2].data_ptr(), _stream(q1)))
+    _run(q1, lib().streamkl_fwd_one_pass, ctypes.byref(p), q1.data_ptr(), k1.data_ptr(),
+         q2.data_ptr(), k2.data_ptr(), out[0].data_ptr(),
+         out[1].data_ptr(), out[2].data_ptr(), _stream(q1))
     return out
 
 
@@ -252,12 +270,12 @@ def streamkl_fwd_fp8(q1, k1, q2, k2, descale1=1.0, descale2=1.0, scale=None, cau
         out = tuple(torch.empty((B, H, nq), dtype=torch.float32, device=q1.device)
                     for _ in range(3))
     for n, t in zip(("kl", "lse1", "lse2"), out):
-        _rowvec(t, n, (B, H, nq))
+        _rowvec(t, n, (B, H, nq), q1.device)
     p = make_problem(q1, k1, scale, causal)
-    _check(lib().streamkl_fwd_fp8(ctypes.byref(p), float(descale1), float(descale2),
-                                  q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(),
-                                  out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
-                                  _stream(q1)))
+    _run(q1, lib().streamkl_fwd_fp8, ctypes.byref(p), float(descale1), float(descale2),
+         q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(),
+         out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
+         _stream(q1))
     return out
 
 
@@ -283,18 +301,19 @@ def streamkl_fwd_splitk(q1, k1, q2, k2, scale=None, causal=False, n_splits=0, wo
         out = tuple(torch.empty((B, H, nq), dtype=torch.float32, device=q1.device)
                     for _ in range(3))
     for n, t in zip(("kl", "lse1", "lse2"), out):
-        _rowvec(t, n, (B, H, nq))
+        _rowvec(t, n, (B, H, nq), q1.device)
     p = make_problem(q1, k1, scale, causal)
     need = int(lib().streamkl_fwd_splitk_workspace_size(ctypes.byref(p), int(n_splits)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous CUDA tensor")
+    _same_device(q1.device, ("workspace", workspace))
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib().streamkl_fwd_splitk(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(),
-                                     q2.data_ptr(), k2.data_ptr(), out[0].data_ptr(),
-                                     out[1].data_ptr(), out[2].data_ptr(), int(n_splits),
-                                     workspace.data_ptr(), nbytes, _stream(q1)))
+    _run(q1, lib().streamkl_fwd_splitk, ctypes.byref(p), q1.data_ptr(), k1.data_ptr(),
+         q2.data_ptr(), k2.data_ptr(), out[0].data_ptr(),
+         out[1].data_ptr(), out[2].data_ptr(), int(n_splits),
+         workspace.data_ptr(), nbytes, _stream(q1))
     return out
 
 
@@ -307,6 +326,7 @@ def _grad_out(q, k, out):
         if not t.is_cuda or t.dtype != torch.bfloat16 or t.shape != ref.shape \
                 or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous bfloat16 CUDA tensor of shape {tuple(ref.shape)}")
+        _same_device(q.device, (n, t))
     return out
 
 
@@ -322,15 +342,15 @@ def streamkl_bwd_fixP1(q1, k1, q2, k2, lse1, lse2, grad_kl, scale=None, causal=F
     _check_inputs(q1, k1, q2, k2)
     B, H, nq, _ = q1.shape
     for n, t in (("lse1", lse1), ("lse2", lse2), ("grad_kl", grad_kl)):
-        _rowvec(t, n, (B, H, nq))
+        _rowvec(t, n, (B, H, nq), q1.device)
     out = _grad_out(q2, k2, out)
     p = make_problem(q1, k1, scale, causal)
     need = int(lib().streamkl_bwd_workspace_size(ctypes.byref(p)))
     wp, wn, _keep = _workspace(need, workspace, q1.device)
-    _check(lib().streamkl_bwd_fixP1(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
-                                    k2.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
-                                    grad_kl.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
-                                    wp, wn, _stream(q1)))
+    _run(q1, lib().streamkl_bwd_fixP1, ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
+         k2.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
+         grad_kl.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
+         wp, wn, _stream(q1))
     return out
 
 
@@ -341,15 +361,15 @@ def streamkl_bwd_fixP2(q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=None, caus
     _check_inputs(q1, k1, q2, k2)
     B, H, nq, _ = q1.shape
     for n, t in (("lse1", lse1), ("lse2", lse2), ("kl", kl), ("grad_kl", grad_kl)):
-        _rowvec(t, n, (B, H, nq))
+        _rowvec(t, n, (B, H, nq), q1.device)
     out = _grad_out(q1, k1, out)
     p = make_problem(q1, k1, scale, causal)
     need = int(lib().streamkl_bwd_workspace_size(ctypes.byref(p)))
     wp, wn, _keep = _workspace(need, workspace, q1.device)
-    _check(lib().streamkl_bwd_fixP2(ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
-                                    k2.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
-                                    kl.data_ptr(), grad_kl.data_ptr(), out[0].data_ptr(),
-                                    out[1].data_ptr(), wp, wn, _stream(q1)))
+    _run(q1, lib().streamkl_bwd_fixP2, ctypes.byref(p), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
+         k2.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
+         kl.data_ptr(), grad_kl.data_ptr(), out[0].data_ptr(),
+         out[1].data_ptr(), wp, wn, _stream(q1))
     return out
 
 
@@ -361,17 +381,19 @@ def _bwd_one(which, setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale, cau
     if setting == 2:
         vecs.append(("kl", kl))
     for n, t in vecs:
-        _rowvec(t, n, (B, H, nq))
+        _rowvec(t, n, (B, H, nq), q1.device)
     ref = (q2 if setting == 1 else q1) if which == "dq" else (k2 if setting == 1 else k1)
     if out is None:
         out = torch.empty(ref.shape, dtype=torch.bfloat16, device=ref.device)
     if out.dtype != torch.bfloat16 or out.shape != ref.shape or not out.is_contiguous():
         raise ValueError(f"{which} must be a contiguous bfloat16 tensor of shape {tuple(ref.shape)}")
+    _same_device(q1.device, (which, out))
     p = make_problem(q1, k1, scale, causal)
     fn = lib().streamkl_bwd_dq if which == "dq" else lib().streamkl_bwd_dk
-    _check(fn(ctypes.byref(p), setting, q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(),
-              lse1.data_ptr(), lse2.data_ptr(), kl.data_ptr() if kl is not None else None,
-              grad_kl.data_ptr(), out.data_ptr(), _stream(q1)))
+    _run(q1, fn, ctypes.byref(p), setting, q1.data_ptr(), k1.data_ptr(), q2.data_ptr(),
+         k2.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
+         kl.data_ptr() if kl is not None else None, grad_kl.data_ptr(), out.data_ptr(),
+         _stream(q1))
     return out
 
 
@@ -409,24 +431,26 @@ def streamkl_bwd_dq_splitk(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, sca
     if setting == 2:
         vecs.append(("kl", kl))
     for n, t in vecs:
-        _rowvec(t, n, (B, H, nq))
+        _rowvec(t, n, (B, H, nq), q1.device)
     ref = q2 if setting == 1 else q1
     if out is None:
         out = torch.empty(ref.shape, dtype=torch.bfloat16, device=ref.device)
     if out.dtype != torch.bfloat16 or out.shape != ref.shape or not out.is_contiguous():
         raise ValueError(f"dq must be a contiguous bfloat16 tensor of shape {tuple(ref.shape)}")
+    _same_device(q1.device, ("dq", out))
     p = make_problem(q1, k1, scale, causal)
     need = int(lib().streamkl_bwd_dq_splitk_workspace_size(ctypes.byref(p), int(n_splits)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous CUDA tensor")
+    _same_device(q1.device, ("workspace", workspace))
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib().streamkl_bwd_dq_splitk(ctypes.byref(p), setting, q1.data_ptr(), k1.data_ptr(),
-                                        q2.data_ptr(), k2.data_ptr(), lse1.data_ptr(),
-                                        lse2.data_ptr(), kl.data_ptr() if kl is not None else None,
-                                        grad_kl.data_ptr(), out.data_ptr(), int(n_splits),
-                                        workspace.data_ptr(), nbytes, _stream(q1)))
+    _run(q1, lib().streamkl_bwd_dq_splitk, ctypes.byref(p), setting, q1.data_ptr(), k1.data_ptr(),
+         q2.data_ptr(), k2.data_ptr(), lse1.data_ptr(),
+         lse2.data_ptr(), kl.data_ptr() if kl is not None else None,
+         grad_kl.data_ptr(), out.data_ptr(), int(n_splits),
+         workspace.data_ptr(), nbytes, _stream(q1))
     return out
 
 
@@ -447,7 +471,7 @@ def streamkl_bwd_fused(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=N
     if setting == 2:
         vecs.append(("kl", kl))
     for n, t in vecs:
-        _rowvec(t, n, (B, H, nq))
+        _rowvec(t, n, (B, H, nq), q1.device)
     qf, kf = (q2, k2) if setting == 1 else (q1, k1)
     if out is None:
         out = (torch.empty(qf.shape, dtype=torch.bfloat16, device=qf.device),
@@ -456,16 +480,18 @@ def streamkl_bwd_fused(setting, q1, k1, q2, k2, lse1, lse2, kl, grad_kl, scale=N
         if t.dtype != torch.bfloat16 or t.shape != ref.shape or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous bfloat16 tensor of shape "
                              f"{tuple(ref.shape)}")
+        _same_device(q1.device, (name, t))
     p = make_problem(q1, k1, scale, causal)
     need = int(lib().streamkl_bwd_fused_workspace_size(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous CUDA tensor")
+    _same_device(q1.device, ("workspace", workspace))
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib().streamkl_bwd_fused(ctypes.byref(p), setting, q1.data_ptr(), k1.data_ptr(),
-                                    q2.data_ptr(), k2.data_ptr(), lse1.data_ptr(),
-                                    lse2.data_ptr(), kl.data_ptr() if kl is not None else None,
-                                    grad_kl.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
-                                    workspace.data_ptr(), nbytes, _stream(q1)))
+    _run(q1, lib().streamkl_bwd_fused, ctypes.byref(p), setting, q1.data_ptr(), k1.data_ptr(),
+         q2.data_ptr(), k2.data_ptr(), lse1.data_ptr(),
+         lse2.data_ptr(), kl.data_ptr() if kl is not None else None,
+         grad_kl.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
+         workspace.data_ptr(), nbytes, _stream(q1))
     return out

@@ -2065,17 +2065,30 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_addr[kMaxDevices] = {};
 
-// Device address of the current device's scratch copy (looked up on the first call per device).
-streamkl_status_t scratch_address(void** out, const char* what) {
+// Device address of the scratch copy on the device that `stream` belongs to (the current device
+// for the null stream), where the kernels of the call run. Looked up on the first call for that
+// device, with that device current (each GPU holds its own copy at its own address).
+streamkl_status_t scratch_address(hipStream_t stream, void** out, const char* what) {
   int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(STREAMKL_ERROR_HIP, std::string(what) + ": hipGetDevice: " + hipGetErrorString(e));
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess)
+    return fail(STREAMKL_ERROR_HIP, std::string(what) + ": hipStreamGetDevice: " + hipGetErrorString(e));
   if (dev < 0 || dev >= kMaxDevices)
     return fail(STREAMKL_ERROR_NOT_SUPPORTED, std::string(what) + ": device index out of range");
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_addr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess)
+      return fail(STREAMKL_ERROR_HIP, std::string(what) + ": hipGetDevice: " + hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(STREAMKL_ERROR_HIP, std::string(what) + ": hipSetDevice: " + hipGetErrorString(e));
     void* ptr = nullptr;
     e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);  // the caller's current device is left as it was
+      if (e == hipSuccess) e = r;
+    }
     if (e != hipSuccess || !ptr)
       return fail(STREAMKL_ERROR_HIP, std::string(what) + ": hipGetSymbolAddress: " + hipGetErrorString(e));
     g_scratch_addr[dev] = ptr;
@@ -2137,7 +2150,7 @@ streamkl_status_t streamkl_fwd_noalloc(const streamkl_problem_t* p, const void* 
   st = check_outputs(p, q1, k1, q2, k2, outs, 3, "streamkl_fwd_noalloc");
   if (st != STREAMKL_SUCCESS) return st;
   void* ws = nullptr;
-  st = scratch_address(&ws, "streamkl_fwd_noalloc");
+  st = scratch_address(stream, &ws, "streamkl_fwd_noalloc");
   if (st != STREAMKL_SUCCESS) return st;
   return fwd_splitk_common(p, q1, k1, q2, k2, kl, lse1, lse2, plan, ws, kScratchBytes, stream,
                            "streamkl_fwd_noalloc");

@@ -204,6 +204,25 @@ def test_invalid_call_raises():
     with pytest.raises(skl.StreamKLError) as e:
         skl.streamkl_fwd(bad, bad, bad, bad)
     assert e.value.status == 2
+    # tensors that are not on the inputs' device are refused by the binding before any call:
+    # an output, a row vector or a workspace in host memory would hand the kernels a host address
+    q1, k1, q2, k2, g = d["q1"], d["k1"], d["q2"], d["k2"], d["g"]
+    kl, l1, l2 = skl.streamkl_fwd(q1, k1, q2, k2)
+    host_bf16 = torch.empty(q2.shape, dtype=torch.bfloat16)
+    for call in (
+            lambda: skl.streamkl_bwd_dq(1, q1, k1, q2, k2, l1, l2, None, g, out=host_bf16),
+            lambda: skl.streamkl_bwd_dk(1, q1, k1, q2, k2, l1, l2, None, g, out=host_bf16),
+            lambda: skl.streamkl_bwd_dq_splitk(1, q1, k1, q2, k2, l1, l2, None, g,
+                                               out=host_bf16),
+            lambda: skl.streamkl_bwd_fused(1, q1, k1, q2, k2, l1, l2, None, g,
+                                           out=(host_bf16, torch.empty_like(k2))),
+            lambda: skl.streamkl_bwd_fixP1(q1, k1, q2, k2, l1, l2, g.cpu()),
+            lambda: skl.streamkl_fwd(q1, k1, q2, k2, out=(kl.cpu(), l1, l2)),
+            lambda: skl.streamkl_fwd_splitk(q1, k1, q2, k2,
+                                            workspace=torch.empty(1 << 20, dtype=torch.uint8)),
+            lambda: skl.streamkl_fwd(q1.cpu(), k1, q2, k2)):
+        with pytest.raises(ValueError):
+            call()
 
 
 def spiky_inputs(B, H, nq, nk, d, boost, seed):

@@ -483,7 +483,7 @@ class ClockSampler:
 
 def extra_hbm_mode(args):
     """Device memory beyond inputs and outputs while the forward and the backward (setting 1)
-    run, at causal N = 16K, 32K, 64K (32 heads, d = 128): the driver's free bytes
+    run, at causal N = 16K, 32K, 64K (32 heads, d = 128): the HIP runtime's free device bytes
     (torch.cuda.mem_get_info, i.e. hipMemGetInfo) before and after, and the allocator's peak
     above the resident tensors. The library allocates nothing and the one-pass paths take no
     workspace, so both must be 0 at every N, against the N^2 bytes that P1 and P2 in bf16 would
@@ -516,7 +516,7 @@ def extra_hbm_mode(args):
         free1, _ = torch.cuda.mem_get_info(dev)
         rows.append({"n": n, "inputs_bytes": 4 * q1.numel() * 2, "saved_state_bytes": 3 * n * H * 4,
                      "gradient_bytes": 2 * q1.numel() * 2,
-                     "driver_free_bytes_change": int(free0 - free1),
+                     "device_free_bytes_change": int(free0 - free1),
                      "allocator_peak_above_resident": int(torch.cuda.max_memory_allocated(dev) -
                                                           resident),
                      "p1_p2_bf16_bytes_avoided": 2 * H * n * n * 2})

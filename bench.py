@@ -163,6 +163,22 @@ def summarize_counters(dirs) -> str:
         co_s = f"{100 * co / busy:.1f} %" if co and busy else "n/a"
         rest = [f"{avg(k, c):.4g}" if avg(k, c) is not None else "n/a" for c in cols[2:]]
         lines.append(f"| {k} | {cyc_s} | {busy_s} | {co_s} | " + " | ".join(rest) + " |")
+    # Wave states, as shares of the waves' lifetime (SQ_WAVE_CYCLES, summed over waves): issuing
+    # an instruction (SQ_ACTIVE_INST_ANY), ready but not issued because the SIMD served another
+    # wave (SQ_WAIT_INST_ANY), and waiting on a dependency, a counter (s_waitcnt) or the barrier
+    # (SQ_WAIT_ANY); the three add up to the lifetime.
+    if any(avg(k, "SQ_WAVE_CYCLES") for k in tot):
+        lines += ["", "| kernel | issuing | ready, SIMD busy with the other wave | waiting on "
+                      "dependencies / counters / barrier | VALU active | LDS active |",
+                  "|---|---|---|---|---|---|"]
+        for k in sorted(tot):
+            life = avg(k, "SQ_WAVE_CYCLES")
+            if not life:
+                continue
+            share = [avg(k, c) for c in ("SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY",
+                                         "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS")]
+            cells = [f"{100 * v / life:.1f} %" if v is not None else "n/a" for v in share]
+            lines.append(f"| {k} | " + " | ".join(cells) + " |")
     return "\n".join(lines)
 
 

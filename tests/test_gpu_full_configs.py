@@ -80,10 +80,20 @@ def oracle_whole_slice(a, g, scale, causal, settings):
     return fwd, dq, dk
 
 
-@pytest.mark.parametrize("name", ["tiny_256_d64", "nc_4k_d128", "causal_16k_sharedk_d128",
-                                  "causal_64k_d128", "asym_2k_32k_d64"])
-def test_full_size(name):
+# each workload with the backward settings it names, and two more: setting 2 at the 64K causal
+# size and setting 1 on the shared-key workload
+CASES = [(n, None) for n in ("tiny_256_d64", "nc_4k_d128", "causal_16k_sharedk_d128",
+                             "causal_64k_d128", "asym_2k_32k_d64")]
+CASES += [("causal_64k_d128", (2,)), ("causal_16k_sharedk_d128", (1,))]
+
+
+@pytest.mark.parametrize("name,settings", CASES,
+                         ids=[n + ("" if st is None else f"_setting{st[0]}") for n, st in CASES])
+def test_full_size(name, settings):
     w = WORKLOADS[name]
+    if settings is not None:
+        import dataclasses
+        w = dataclasses.replace(w, settings=settings)
     announce(f"[full] {name}: generating inputs")
     x = make_inputs(w)
     d = {n: dev_bf16(x[n]) for n in ("q1", "k1", "q2")}

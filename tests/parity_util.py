@@ -71,3 +71,48 @@ def assert_grad_close(got, ref, what, atol=0.0, extra=None):
     nerr, nref = np.linalg.norm(got - ref), np.linalg.norm(ref)
     assert nerr <= GRAD_RTOL * nref + atol * np.sqrt(ref.size), \
         f"{what}: normwise error {nerr:.3e} vs reference norm {nref:.3e}"
+
+
+def row_chunks(n_q, n_k, causal, n_chunks):
+    """Contiguous row ranges with about equal numbers of visible pairs."""
+    pairs = np.minimum(np.arange(n_q) + 1, n_k) if causal else np.full(n_q, n_k)
+    cum = np.cumsum(pairs)
+    cuts = np.searchsorted(cum, np.linspace(0, cum[-1], n_chunks + 1)[1:-1])
+    edges = np.unique(np.concatenate([[0], cuts, [n_q]]))
+    return [np.arange(a, b) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+
+
+def oracle_forward_rows(a, scale, causal, rows=None):
+    """The oracle's KL, LSE1, LSE2 ([3, len(rows)]) of one slice (a: q1, k1, q2, k2 in float64)
+    for the given query rows (default: all), over row blocks in a thread pool with BLAS at one
+    thread per worker (the rows of a block are independent)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle.reference import forward_slice
+
+    n_q, n_k = a["q1"].shape[0], a["k1"].shape[0]
+    rows = np.arange(n_q) if rows is None else np.asarray(rows)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    if len(rows) == n_q:
+        chunks = row_chunks(n_q, n_k, causal, 8 * workers)
+    else:
+        chunks = np.array_split(rows, max(1, min(len(rows), workers)))
+    out = np.empty((3, n_q))
+
+    def run(r):
+        return r, forward_slice(a["q1"], a["k1"], a["q2"], a["k2"], scale, causal, rows=r)
+
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        ctx = None
+    try:
+        with ThreadPoolExecutor(workers) as ex:
+            for r, f in ex.map(run, chunks):
+                out[:, r] = np.stack(f)
+    finally:
+        if ctx is not None:
+            ctx.restore_original_limits()
+    return out[:, rows]

@@ -6,8 +6,8 @@ import torch
 
 import online_attention_kl_amd as skl
 import oracle
-from parity_util import assert_rows_close, to_np
-from workloads import Workload, fp8_e4m3_bits_to_f32, fp8_inputs
+from parity_util import assert_rows_close, oracle_forward_rows, to_np
+from workloads import WORKLOADS, Workload, fp8_e4m3_bits_to_f32, fp8_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -68,3 +68,35 @@ def test_fp8_rejects_bad_descale_and_stride():
         skl.streamkl_fwd_fp8(q, k, q, k, 0.0, 1.0)
     with pytest.raises(skl.StreamKLError):
         skl.streamkl_fwd_fp8(q, k, q, k, float("inf"), 1.0)
+
+
+@pytest.mark.parametrize("name", ["nc_4k_d128", "causal_64k_d128"])
+def test_fp8_full_size(name):
+    """The fp8 forward on a whole workload (its inputs scaled by the gains and rounded to e4m3,
+    as bench.py --fp8 times it): every row of slice (0, 0) and sampled rows of two more slices
+    against the oracle on the exactly decoded inputs."""
+    w = WORKLOADS[name]
+    print(f"fp8 full size {name}: generating inputs", flush=True)
+    x = fp8_inputs(w, GAIN)
+    dv = {n: dev_fp8(x[n]) for n in ("q1", "k1", "q2")}
+    dv["k2"] = dv["k1"] if x["k2"] is x["k1"] else dev_fp8(x["k2"])
+    kl, l1, l2 = skl.streamkl_fwd_fp8(dv["q1"], dv["k1"], dv["q2"], dv["k2"], x["descale1"],
+                                      x["descale2"], causal=w.causal)
+    kl_h, l1_h, l2_h = to_np(kl), to_np(l1), to_np(l2)
+    rng = np.random.default_rng(11)
+    B, H = w.batch, w.heads
+    slices = [(0, 0)] + sorted({(B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))}
+                               - {(0, 0)})
+    for b, h in slices:
+        print(f"fp8 full size {name}: oracle on slice ({b}, {h})", flush=True)
+        a = {n: fp8_e4m3_bits_to_f32(x[n][b, h]).astype(np.float64) / gn
+             for n, gn in zip(("q1", "k1", "q2", "k2"), GAIN)}
+        if (b, h) == (0, 0):
+            rows = np.arange(w.n_q)
+        else:
+            rows = np.unique(np.concatenate([[0, 1, w.n_q // 2, w.n_q - 2, w.n_q - 1],
+                                             rng.integers(0, w.n_q, 24)]))
+        rk, r1, r2 = oracle_forward_rows(a, w.scale, w.causal, rows)
+        assert_rows_close(kl_h[b, h, rows], rk, f"{name} fp8 KL ({b}, {h})")
+        assert_rows_close(l1_h[b, h, rows], r1, f"{name} fp8 LSE1 ({b}, {h})")
+        assert_rows_close(l2_h[b, h, rows], r2, f"{name} fp8 LSE2 ({b}, {h})")

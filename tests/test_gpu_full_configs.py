@@ -19,7 +19,8 @@ import torch
 
 import online_attention_kl_amd as skl
 from oracle.reference import backward_slice, forward_slice
-from parity_util import assert_grad_close, assert_rows_close, dev_bf16, f64, grad_atol
+from parity_util import (assert_grad_close, assert_rows_close, dev_bf16, f64, grad_atol,
+                         row_chunks)
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -34,15 +35,6 @@ def sampled_rows(n, rng, k=24):
     base = {0, 1, n - 1, n - 2, n // 2}
     base |= set(rng.integers(0, n, size=k).tolist())
     return np.array(sorted(x for x in base if 0 <= x < n))
-
-
-def row_chunks(n_q, n_k, causal, n_chunks):
-    """Contiguous row ranges with about equal numbers of visible pairs."""
-    pairs = np.minimum(np.arange(n_q) + 1, n_k) if causal else np.full(n_q, n_k)
-    cum = np.cumsum(pairs)
-    cuts = np.searchsorted(cum, np.linspace(0, cum[-1], n_chunks + 1)[1:-1])
-    edges = np.unique(np.concatenate([[0], cuts, [n_q]]))
-    return [np.arange(a, b) for a, b in zip(edges[:-1], edges[1:]) if b > a]
 
 
 def oracle_whole_slice(a, g, scale, causal, settings):

@@ -45,7 +45,7 @@ EXP2_SLOTS = 2
 VALU_WORK = {"fwd": (6.0, 2), "bwd1": (3.5, 2), "bwd2": (4.5, 1)}
 KERNEL_SOURCE = os.path.join(ROOT, "online_attention_kl_amd", "csrc", "streamkl_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-SMALL_NQ_ROUNDS = 3  # interleaved timing rounds of --small-nq (fastest round kept per path)
+SMALL_NQ_ROUNDS = 4  # interleaved timing rounds of --small-nq (fastest round kept per path)
 
 
 def source_sha() -> str:
@@ -322,14 +322,21 @@ def small_nq(args):
         fns["fwd_auto"] = lambda: skl.streamkl_fwd(q1, k1, q2, k2, out=out, workspace=wsa_f)
         fns["bwd_auto"] = lambda: skl.streamkl_bwd_fixP1(q1, k1, q2, k2, l1, l2, g, out=(dq, dk),
                                                          workspace=wsa_b)
-        # every path is timed in SMALL_NQ_ROUNDS interleaved rounds and keeps its fastest round,
-        # so that no path's figure depends on which path ran just before it
+        # every path is timed in SMALL_NQ_ROUNDS interleaved rounds, the order rotated by one
+        # path per round, and keeps its fastest round: a path timed right after the long,
+        # low-occupancy one-pass kernels measured up to ~9 % slower than the same kernels timed
+        # elsewhere, so no path may always follow the same one
         ms = {}
         for name, fn in fns.items():
             for _ in range(args.warmup):
                 fn()
-        for _ in range(SMALL_NQ_ROUNDS):
-            for name, fn in fns.items():
+        order = list(fns.items())
+        for rnd in range(SMALL_NQ_ROUNDS):
+            for name, fn in order[rnd % len(order):] + order[:rnd % len(order)]:
+                # two untimed calls of this path first: the timed calls never follow another
+                # path's launches directly
+                fn()
+                fn()
                 torch.cuda.synchronize()
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)

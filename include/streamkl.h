@@ -126,7 +126,7 @@ streamkl_status_t streamkl_fwd_one_pass(const streamkl_problem_t* problem, const
  * the process ends) instead of a caller buffer. The call allocates nothing and frees nothing.
  * Limit: the split-K partial states must fit in streamkl_fwd_noalloc_max_workspace() bytes
  * (4 MiB). The default plan never needs more than 3.75 MiB (at most 256 work items unsplit, cut
- * into about 512 block items of 256 query rows or 4096 wavefront items of 32 rows, 5 floats per
+ * into about 512 block items of 256 query rows or 1024 wavefront items of 32 rows, 5 floats per
  * row and key range), so every size runs; a plan beyond the scratch would return
  * STREAMKL_ERROR_NOT_SUPPORTED and enqueue nothing. The one-pass path needs no scratch.
  * Every call on a GPU shares that GPU's scratch: calls that may overlap on one GPU (several
@@ -183,7 +183,7 @@ streamkl_status_t streamkl_fwd_fp8(const streamkl_problem_t* problem, float desc
  * Errors: as streamkl_fwd, plus STREAMKL_ERROR_INVALID_VALUE for a NULL, misaligned,
  *   overlapping or too small workspace.
  */
-/* Number of key ranges chosen for n_splits <= 0: about 4096 wavefront work items (n_q <= 32)
+/* Number of key ranges chosen for n_splits <= 0: about 1024 wavefront work items (n_q <= 32)
  * or 512 block work items (n_q > 32), with at least 8 key granules per range (only keys some
  * row can see count when causal); 1 when there are more than 256 work items without splitting,
  * where streamkl_fwd is the faster path. 0 for a NULL problem or sizes < 1. */
@@ -299,7 +299,7 @@ streamkl_status_t streamkl_bwd_dk(const streamkl_problem_t* problem, int32_t set
  * Other arguments and errors as streamkl_bwd_dq, plus STREAMKL_ERROR_INVALID_VALUE for a too
  * small, misaligned or overlapping workspace.
  */
-/* Ranges chosen for n_splits <= 0: about two blocks per CU with at least 16 key tiles per range;
+/* Ranges chosen for n_splits <= 0: about one block per CU with at least 16 key tiles per range;
  * 1 when the dQ kernel already has 256 blocks or more. 0 for a NULL problem or sizes < 1. */
 int32_t streamkl_bwd_dq_splitk_default_splits(const streamkl_problem_t* problem);
 /* Workspace bytes streamkl_bwd_dq_splitk needs for this n_splits (0 with one range, and for a

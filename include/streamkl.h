@@ -331,8 +331,8 @@ streamkl_status_t streamkl_bwd_dq_splitk(const streamkl_problem_t* problem, int3
  * workspace: at least streamkl_bwd_fused_workspace_size(problem) bytes of device memory,
  *   16-byte aligned, owned by the caller, overlapping no input or output; contents on entry
  *   ignored, on return unspecified. It holds float32 [ceil(n_k / (128 G))][batch * heads][n_q]
- *   [head_dim], where G, the 32-key groups per wave, is floor(S * batch * heads / 512) clamped to
- *   [1, min(64, S)] with S = ceil(n_k / 128) (about two blocks per CU).
+ *   [head_dim], where G, the 32-key groups per wave, is floor(S * batch * heads / 256) clamped to
+ *   [1, min(64, S)] with S = ceil(n_k / 128) (about one block per CU).
  * Errors: as streamkl_bwd_fixP1 / _fixP2; STREAMKL_ERROR_NOT_SUPPORTED for n_q > 64;
  * STREAMKL_ERROR_INVALID_VALUE for a bad setting or a too small, misaligned or overlapping
  * workspace.

@@ -254,7 +254,7 @@ def test_fused_workspace_and_limits():
         p = good_problem(d)
         p.n_q, p.n_k, p.heads = nq, nk, heads
         steps = -(-nk // 128)
-        groups = max(1, min(64, steps, steps * heads // 512))
+        groups = max(1, min(64, steps, steps * heads // 256))
         nkb = -(-nk // (128 * groups))
         assert L.streamkl_bwd_fused_workspace_size(ctypes.byref(p)) == nkb * heads * nq * d * 4
     p = good_problem()

@@ -23,14 +23,17 @@
 //  * The dK kernel is key-major: a wave keeps its 32 key rows of K1 and K2 in registers and
 //    computes S = Q K^T, so dS^T comes out of the accumulator already in the A-operand layout
 //    of dK = dS^T Q. Symmetrically, the dQ kernel's dS is the A operand of dQ = dS K. The other
-//    operand of each gradient product is read from a transposed copy of the streamed tile that
-//    the block writes to LDS once per tile. The two backward kernels recompute S independently
-//    and never use atomics: results are deterministic.
-//  * Streamed tiles sit in double-buffered LDS with rows padded by 16 bytes, so the 16 rows read
-//    by one 16-byte operand load fall in distinct banks and every operand address is a base
-//    register plus an immediate. They are loaded from HBM through buffer resources (scalar base
-//    and byte range per stage, 32-bit per-thread offsets); the range check pads the ragged end
-//    with zero rows.
+//    operand of each gradient product is read by columns from the streamed tile with the
+//    transposing LDS read. The two backward kernels recompute S independently and never use
+//    atomics: results are deterministic.
+//  * Streamed tiles are loaded from HBM through buffer resources (scalar base and byte range per
+//    stage, 32-bit per-thread offsets); the range check pads the ragged end with zero rows. The
+//    forward stages its key tiles through registers into double-buffered LDS with rows padded by
+//    16 bytes, so the 16 rows read by one 16-byte operand load fall in distinct banks. The
+//    backward kernels load their tiles straight into three LDS stages (buffer loads that write
+//    LDS), rows unpadded with their 16-byte chunks permuted so that both the row reads and the
+//    transposing reads are free of bank conflicts. Every operand address is a register plus an
+//    immediate.
 //  * exp and log use the hardware base-2 instructions; scale * log2(e) is folded into one FMA
 //    per element and the saved LSEs stay in natural-log units.
 //  * Causal (top-left) masking skips whole tiles past the frontier; only tiles that straddle
@@ -721,111 +724,160 @@ fwd_merge_kernel(const float* __restrict__ part, float* __restrict__ kl_out,
 
 // ================================================================ backward
 // Both backward kernels stream 32-row tiles of the "other" side (key rows for the dQ kernel,
-// query rows for the dK kernel) through double-buffered LDS, one barrier per tile, with 8 waves
-// of 32 stationary rows each. A streamed tile is kept twice when it belongs to the free side:
-// row-major (operand of the S recomputation, contraction over head_dim) and transposed (operand
-// of the gradient product, contraction over the streamed rows). The transposed copy stores row r
-// of the tile at column tpos(r) (bits 2 and 3 of r swapped) so that lane half h of a 32x32x16
-// MFMA reads its eight rows 16c + {4h..4h+3, 8+4h..8+4h+3} as one contiguous 16-byte chunk:
-// the order in which a 32x32 accumulator holds rows (acc_row), which makes the accumulator of
-// dS directly the A operand of the gradient product.
+// query rows for the dK kernel) through three LDS stages, one barrier per tile, with 8 waves of
+// 32 stationary rows each. The S recomputation reads a streamed tile's rows (contraction over
+// head_dim); the gradient product reads the free side's tile by columns (contraction over the
+// streamed rows), in the order in which a 32x32 accumulator holds rows (acc_row), which makes
+// the accumulator of dS directly the A operand of that product.
 constexpr int kBwdWaves = 8;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdBlocksPerCU = 8 / kBwdWaves;  // 2 waves per SIMD
-constexpr int kBwdRB = 1;                // 32-row blocks per streamed tile
-constexpr int kBT = 32 * kBwdRB;         // streamed rows per tile
-constexpr int kTPitch = kBT + 8;     // pitch (elements) of a transposed tile
+constexpr int kBT = 32;                          // streamed rows per tile
+
+// Transposed copies (the fused backward's query rows and keys): row r of a 32-row block is
+// stored at column tpos(r) (bits 2 and 3 of r swapped), so that lane half h of a 32x32x16 MFMA
+// reads its eight rows 16c + {4h..4h+3, 8+4h..8+4h+3} as one contiguous 16-byte chunk.
+constexpr int kTPitch = kBT + 8;  // pitch (elements) of a transposed block
 
 __device__ __forceinline__ int tpos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// Value of lane l ^ 1 (DPP quad permutation [1, 0, 3, 2]: a VALU move, no LDS round trip).
-__device__ __forceinline__ unsigned swap_pair(unsigned x) {
-  return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
-}
-
-template <int D>
-struct BwdLayout {
-  static constexpr int RM = kBT * lds_pitch<D>();  // one row-major tile (elements)
-  static constexpr int TR = D * kTPitch;           // one transposed tile (elements)
-};
-
-// Staging of the NT streamed tensors of one tile (tensor 0 = side 1, tensor 1 = side 2; one
-// tensor when K is shared). Chunk assignment is column-major (row = id % 32) so that the two
-// rows of a pair (r, r ^ 1) sit in neighbouring lanes for the transposed store.
-template <int D, int NTENS>
-struct BwdStage {
-  static constexpr int CPR = D / 8;
-  static constexpr int PER = kBT * CPR;                          // chunks per tensor
-  static constexpr int N = (NTENS * PER + kBwdThreads - 1) / kBwdThreads;
-  uint4 v[N];
-
-  __device__ __forceinline__ bool mine(int i, int& te, int& row, int& chunk) const {
-    const int gid = threadIdx.x + i * kBwdThreads;
-    // when a tensor's chunks are a whole number of block-widths, chunk i of every thread belongs
-    // to tensor i * kBwdThreads / PER: known at compile time, so no per-lane branch on it
-    te = PER % kBwdThreads == 0 ? (i * kBwdThreads) / PER : gid / PER;
-    const int rem = gid - te * PER;
-    row = rem % kBT;
-    chunk = rem / kBT;
-    return NTENS * PER % kBwdThreads == 0 || gid < NTENS * PER;  // every thread has N chunks
-  }
-  // Rows row0.. of two [n_valid, D] matrices with a row stride of rstride elements
-  // (< kMaxRowStrideBytes / 2); rows >= n_valid read as 0.
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ b0,
-                                       const uint16_t* __restrict__ b1, long long rstride,
-                                       int row0, int n_valid) {
-    static_assert(PER % 64 == 0, "a wave's chunks belong to one tensor");
-    const __amdgpu_buffer_rsrc_t r0 =
-        make_rsrc<kBT>(b0 + (long long)row0 * rstride, n_valid - row0, rstride * 2);
-    const __amdgpu_buffer_rsrc_t r1 =
-        make_rsrc<kBT>(b1 + (long long)row0 * rstride, n_valid - row0, rstride * 2);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      int te, row, chunk;
-      if (!mine(i, te, row, chunk)) {
-        v[i] = make_uint4(0u, 0u, 0u, 0u);  // never stored
-        continue;
-      }
-      // the tensor index is the same for the whole wave: choose the resource as a scalar
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_readfirstlane(te) == 0 ? r0 : r1;
-      v[i] = buffer_load16(r, (unsigned)row * (unsigned)(rstride * 2) + (unsigned)chunk * 16u, 0u);
-    }
-  }
-  // Row-major copies of every tensor; transposed copy of tensor `free_te`.
-  __device__ __forceinline__ void store(uint16_t* rm0, uint16_t* rm1, uint16_t* tr,
-                                        int free_te) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      int te, row, chunk;
-      if (!mine(i, te, row, chunk)) continue;
-      uint16_t* rm = te == 0 ? rm0 : rm1;
-      *reinterpret_cast<uint4*>(rm + row * lds_pitch<D>() + chunk * 8) = v[i];
-      if (te == free_te) {
-        // lanes l (row r even) and l ^ 1 (row r + 1) swap their chunks; the even lane writes
-        // head_dim columns chunk*8 + 0..3, the odd one chunk*8 + 4..7, each as (r, r+1) pairs
-        const uint4 o = make_uint4(swap_pair(v[i].x), swap_pair(v[i].y), swap_pair(v[i].z),
-                                   swap_pair(v[i].w));
-        const bool odd = row & 1;
-        const uint4 lo = odd ? o : v[i];   // row r even
-        const uint4 hi = odd ? v[i] : o;   // row r + 1
-        const unsigned a0 = odd ? lo.z : lo.x, a1 = odd ? lo.w : lo.y;
-        const unsigned b0 = odd ? hi.z : hi.x, b1 = odd ? hi.w : hi.y;
-        const int d0 = chunk * 8 + (odd ? 4 : 0);
-        unsigned* t = reinterpret_cast<unsigned*>(tr + d0 * kTPitch + tpos(row & ~1));
-        constexpr int P = kTPitch / 2;  // pitch in dwords
-        t[0 * P] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
-        t[1 * P] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
-        t[2 * P] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
-        t[3 * P] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
-      }
-    }
-  }
-};
-
-// B operand of the gradient product: transposed tile rows (head_dim) nb*32 + (l & 31), the
+// B operand of a gradient product from a transposed block: rows (head_dim) nb*32 + (l & 31), the
 // eight streamed rows of chunk cc for lane half h.
 __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tr, int nb, int cc, int col, int h) {
   return load_frag(tr + (nb * 32 + col) * kTPitch + cc * 16 + h * 8);
+}
+
+// ---------------------------------------------------------------- streamed tiles, direct to LDS
+// The backward kernels stream 32-row tiles of the other side's bf16 matrices. A tile goes from
+// global memory straight into LDS (buffer loads with an LDS destination: no registers and no LDS
+// store instructions), three stages deep, so a stage is loaded two tiles ahead of its use. Rows
+// are unpadded (2 D bytes) and the 16-byte chunk c of row r sits at chunk position
+// c ^ bwd_swz(r). The permutation keeps both operand reads free of LDS bank conflicts: the 16-byte
+// row reads of the S recomputation (16 consecutive rows at one chunk per pass) and the 8-byte
+// transposing reads (ds_read_b64_tr_b16; per 32 lanes four consecutive rows by four chunks) that
+// give the gradient product its operand, columns of the row-major tile, with no transposed copy.
+template <int D>
+__device__ __forceinline__ int bwd_swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// LDS byte address (as M0 and the DS instructions take it) of a pointer into a __shared__ array.
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from byte offset voff of resource r to LDS byte address lds + 16 * lane (a
+// buffer load with an LDS destination; M0 holds the wave's LDS address, one wait state before
+// the load reads it, and is restored afterwards: the compiler reserves M0 and does not expect
+// inline assembly to change it). Written as inline assembly so that the compiler does not track
+// it as an LDS write: it would wait for every such load before any later LDS read, the loads of
+// stages prefetched for later tiles included. The kernels wait for these loads themselves
+// (vmcnt) before the barrier that publishes a stage; the loads write no registers.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(lds)
+      : "memory");
+}
+
+// Waits until at most `keep` (0, 1 or 2; wave-uniform) vector memory loads of the wave are in
+// flight (s_waitcnt vmcnt; expcnt and lgkmcnt not waited on), then keeps the compiler from moving
+// memory accesses above the wait.
+__device__ __forceinline__ void wait_loads_keep(int keep) {
+  if (keep >= 2)
+    __builtin_amdgcn_s_waitcnt(0x0F72);
+  else if (keep == 1)
+    __builtin_amdgcn_s_waitcnt(0x0F71);
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
+
+// Direct-to-LDS staging of the NTENS streamed tensors of one tile: each tensor's tile is cut into
+// 1 KB pieces (4 rows at d = 128), piece i loaded by wave i % 8.
+template <int D, int NTENS>
+struct BwdDma {
+  static constexpr int TB = 32 * 2 * D;        // bytes of one tensor's tile
+  static constexpr int PPT = TB / 1024;        // pieces per tensor
+  static constexpr int PIECES = NTENS * PPT;
+  static constexpr int N = (PIECES + kBwdWaves - 1) / kBwdWaves;  // loads per wave, at most
+  static_assert(N <= 2, "wait_loads_keep covers two loads per wave and stage");
+  static constexpr int STAGE = NTENS * TB;     // bytes of one stage
+  unsigned voff[N];  // the lane's byte offset, from the tile's first row, for each load
+  int cnt;           // the wave's loads per tile (wave-uniform)
+
+  __device__ __forceinline__ void init(long long rstride_bytes) {
+    const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
+    cnt = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = w + j * kBwdWaves;
+      const int o = (idx % PPT) * 1024 + 16 * l;  // byte of the lane's 16 bytes in the tile
+      const int row = o / (2 * D), c = ((o % (2 * D)) / 16) ^ bwd_swz<D>(row);
+      voff[j] = (unsigned)row * (unsigned)rstride_bytes + 16u * (unsigned)c;
+      cnt += idx < PIECES ? 1 : 0;
+    }
+  }
+  // Rows row0 .. row0 + 31 of two [n_valid, D] matrices (row stride rstride elements) into the
+  // stage at LDS byte address `stage`; rows >= n_valid read as 0.
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ b0,
+                                        const uint16_t* __restrict__ b1, long long rstride,
+                                        int row0, int n_valid, unsigned stage) const {
+    const __amdgpu_buffer_rsrc_t r0 =
+        make_rsrc<kBT>(b0 + (long long)row0 * rstride, n_valid - row0, rstride * 2);
+    const __amdgpu_buffer_rsrc_t r1 =
+        NTENS == 2 ? make_rsrc<kBT>(b1 + (long long)row0 * rstride, n_valid - row0, rstride * 2)
+                   : r0;
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = w + j * kBwdWaves;
+      if (PIECES % kBwdWaves == 0 || idx < PIECES) {
+        const int te = idx / PPT;
+        lds_dma16(te == 0 ? r0 : r1, voff[j], stage + (unsigned)(te * TB + (idx % PPT) * 1024));
+      }
+    }
+  }
+  // Waits for this wave's loads of every stage but the `pending` (0 or 1) issued last.
+  __device__ __forceinline__ void wait(int pending) const { wait_loads_keep(pending * cnt); }
+};
+
+// A operand of the S recomputation from a swizzled tile: row `row` (0..31), head_dim values
+// kk * 16 + h * 8 .. + 7. a_base = row * 2D + 16 * (h ^ bwd_swz(row)); the chunk's position is
+// then a_base ^ 32 kk (the XOR touches only the bits below the row's).
+__device__ __forceinline__ bf16x8 swz_a_frag(const unsigned char* tile, int a_base, int kk) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tile + (a_base ^ (32 * kk))));
+}
+
+// Per-lane byte offsets of the transposing reads (ds_read_b64_tr_b16). In each group of 16
+// lanes, lane j receives element j % 4 of the 8 bytes read by lanes 4 e + j / 4 (e = 0..3) as
+// its elements e. For the B operand of a gradient product (lane l: tile rows
+// acc_row(8 cc + i, h), i = 0..7, at column nb * 32 + (l & 31)), lane (e = (l >> 2) & 3,
+// m = l & 3) of group g reads row 8 r + 4 h + e (r = 0, 1 for elements 0..3 and 4..7) at
+// columns 16 (g & 1) + 4 m .. + 3; tb[r] is that offset for cc = 0 and nb = 0, column block
+// nb is at tb[r] ^ 64 nb and cc = 1 sixteen rows further.
+template <int D>
+__device__ __forceinline__ void tr_bases(int l, int (&tb)[2]) {
+  const int h = l >> 5, e = (l >> 2) & 3, m = l & 3;
+  const int low = 2 * ((l >> 4) & 1) + (m >> 1);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 8 * r + 4 * h + e;
+    tb[r] = row * 2 * D + 8 * (m & 1) + 16 * (low ^ bwd_swz<D>(row));
+  }
+}
+
+// B operand of a gradient product for column block nb, chunk cc; `tile` points at the tile's
+// first row for cc = 0 and 16 rows further for cc = 1.
+__device__ __forceinline__ bf16x8 swz_tr_frag(const unsigned char* tile, const int (&tb)[2], int nb) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + (tb[0] ^ (64 * nb))));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + (tb[1] ^ (64 * nb))));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // ---------------------------------------------------------------- dQ (query-major)
@@ -845,9 +897,8 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   constexpr int BQ = 32 * kBwdWaves, KS = D / 16, NB = D / 32;
   constexpr int NTENS = SHARED_K ? 1 : 2;
   constexpr int FREE = SHARED_K ? 0 : 2 - SETTING;  // tensor index of K_free (side 2 for setting 1)
-  using L = BwdLayout<D>;
-  constexpr int BUF = NTENS * L::RM + L::TR;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
+  using DM = BwdDma<D, NTENS>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[3 * DM::STAGE];
   __shared__ float gscale[kBwdWaves][32];
 
   int rank, slice;
@@ -894,59 +945,52 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dq[nb] = f32x16{};
 
-  BwdStage<D, NTENS> st;
-  auto stage_store = [&](int buf) {
-    uint16_t* base = lds + buf * BUF;
-    st.store(base, base + (NTENS - 1) * L::RM, base + NTENS * L::RM, FREE);
-  };
-  if (t0 < t1) {
-    st.load(K1, K2, s.k_sr, t0 * kBT, s.nk);
-    stage_store(0);
-    if (t0 + 1 < t1) st.load(K1, K2, s.k_sr, (t0 + 1) * kBT, s.nk);
-  }
+  // per-lane offsets of the operand reads in a stage (S recomputation and transposing reads)
+  const int a_base = col * 2 * D + 16 * (h ^ bwd_swz<D>(col));
+  int tb[2];
+  tr_bases<D>(l, tb);
+  DM dma;
+  dma.init(s.k_sr * 2);
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
+  const int n = t1 - t0;
+  if (n > 0) dma.issue(K1, K2, s.k_sr, t0 * kBT, s.nk, lds0);
+  if (n > 1) dma.issue(K1, K2, s.k_sr, (t0 + 1) * kBT, s.nk, lds0 + DM::STAGE);
+  dma.wait(n > 1 ? 1 : 0);
   __syncthreads();
 
-  for (int t = t0; t < t1; ++t) {
-    const uint16_t* base = lds + ((t - t0) & 1) * BUF;
-    const uint16_t* kt1 = base;
-    const uint16_t* kt2 = base + (NTENS - 1) * L::RM;
-    const uint16_t* ktr = base + NTENS * L::RM;
+  // one tile; the loop is unrolled three times so that the stage (i % 3) is a compile-time
+  // constant and every operand read is a per-lane register plus an immediate offset
+  auto tile = [&](int i, auto stgc) {
+    constexpr int STG = decltype(stgc)::value;
+    const int t = t0 + i;
+    if (i + 2 < n) dma.issue(K1, K2, s.k_sr, (t + 2) * kBT, s.nk, lds0 + ((STG + 2) % 3) * DM::STAGE);
+    const unsigned char* stage = lds + STG * DM::STAGE;
+    const unsigned char* kt1 = stage;
+    const unsigned char* kt2 = stage + (NTENS - 1) * DM::TB;
+    const unsigned char* ktr = stage + FREE * DM::TB;
     const int key0 = t * kBT;
     const bool skip = !wave_live || (CAUSAL && key0 > qw0 + 31);
     if (!skip) {
-      // S^T for the tile's kBwdRB key blocks: 2 * kBwdRB independent accumulation chains
-      f32x16 x1[kBwdRB], x2[kBwdRB];
-#pragma unroll
-      for (int rb = 0; rb < kBwdRB; ++rb) {
-        x1[rb] = f32x16{};
-        x2[rb] = f32x16{};
-      }
+      // S^T of the tile's 32 keys: 2 independent accumulation chains
+      f32x16 x1 = f32x16{}, x2 = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        bf16x8 a1[kBwdRB], a2[kBwdRB];
-#pragma unroll
-        for (int rb = 0; rb < kBwdRB; ++rb) {
-          a1[rb] = lds_a_frag<D>(kt1, rb * 32 + col, kk, h);
-          if (!SHARED_K) a2[rb] = lds_a_frag<D>(kt2, rb * 32 + col, kk, h);
-        }
-#pragma unroll
-        for (int rb = 0; rb < kBwdRB; ++rb) {
-          x1[rb] = mfma(a1[rb], f1[kk], x1[rb]);
-          x2[rb] = mfma(SHARED_K ? a1[rb] : a2[rb], f2[kk], x2[rb]);
-        }
+        const bf16x8 a1 = swz_a_frag(kt1, a_base, kk);
+        const bf16x8 a2 = SHARED_K ? a1 : swz_a_frag(kt2, a_base, kk);
+        x1 = mfma(a1, f1[kk], x1);
+        x2 = mfma(a2, f2[kk], x2);
       }
-      // dS of one 32-key block and its dQ product; the element mask is compiled only into the
+      // dS of the 32-key block and its dQ product; the element mask is compiled only into the
       // variant used on tiles that straddle the diagonal or the ragged end
-      auto ds_block = [&](auto maskc, int rb) {
+      auto ds_block = [&](auto maskc) {
         constexpr bool MASK = decltype(maskc)::value;
-        const int kb0 = key0 + rb * 32;
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float e1 = x1[rb][r], e2 = x2[rb][r];
+          float e1 = x1[r], e2 = x2[r];
           const float d12 = e1 - e2;
           if (MASK) {
-            const int key = kb0 + acc_row(r, h);
+            const int key = key0 + acc_row(r, h);
             const bool ok = key < s.nk && (!CAUSAL || key <= query);
             e1 = ok ? e1 : -kInf;
             e2 = ok ? e2 : -kInf;
@@ -962,23 +1006,24 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           const bf16x8 a = pack8(ds + 8 * cc);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            dq[nb] = mfma(a, tr_frag(ktr, nb, rb * 2 + cc, col, h), dq[nb]);
+            dq[nb] = mfma(a, swz_tr_frag(ktr + cc * 32 * D, tb, nb), dq[nb]);
         }
       };
-#pragma unroll
-      for (int rb = 0; rb < kBwdRB; ++rb) {
-        const int kb0 = key0 + rb * 32;
-        if (lane_flag((kb0 + 32 <= s.nk) && (!CAUSAL || kb0 + 31 <= qw0)))
-          ds_block(std::false_type{}, rb);
-        else
-          ds_block(std::true_type{}, rb);
-      }
+      if (lane_flag((key0 + 32 <= s.nk) && (!CAUSAL || key0 + 31 <= qw0)))
+        ds_block(std::false_type{});
+      else
+        ds_block(std::true_type{});
     }
-    if (t + 1 < t1) {
-      stage_store((t + 1 - t0) & 1);
-      if (t + 2 < t1) st.load(K1, K2, s.k_sr, (t + 2) * kBT, s.nk);
-    }
+    if (i + 1 < n) dma.wait(i + 2 < n ? 1 : 0);
     __syncthreads();
+  };
+  for (int i = 0; i < n;) {
+    tile(i, std::integral_constant<int, 0>{});
+    if (++i >= n) break;
+    tile(i, std::integral_constant<int, 1>{});
+    if (++i >= n) break;
+    tile(i, std::integral_constant<int, 2>{});
+    ++i;
   }
   if (!wave_live) return;
   const long long obase = (long long)slice * s.nq;
@@ -1031,14 +1076,15 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           __bf16* __restrict__ dk_out, Shape s) {
   constexpr int BKW = 32 * kBwdWaves, KS = D / 16, NB = D / 32;
   constexpr int FREE = 2 - SETTING;  // tensor index of Q_free (side 2 for setting 1)
-  using L = BwdLayout<D>;
-  constexpr int BUF = 2 * L::RM + L::TR;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
-  // Per query of a tile: the exponent bias of P1 and of P2 (setting 1) or LSE2 - LSE1 - KL
-  // (setting 2), with log2 |g| folded into the exponent biases (g P = sign(g) 2^(y + log2 |g|)),
-  // and sign(g). Tiles whose g are all >= 0 (flag qneg = 0) never read the sign.
-  __shared__ __attribute__((aligned(16))) float qa[2][3][kBT];
-  __shared__ int qneg[2];
+  using DM = BwdDma<D, 2>;
+  constexpr int NRAW = SETTING == 1 ? 3 : 4;  // per-query inputs: LSE1, LSE2, g (and KL)
+  __shared__ __attribute__((aligned(16))) unsigned char lds[3 * DM::STAGE];
+  // Per stage, the constants wave 0 makes from the tile's per-query inputs: per query the
+  // exponent bias of P1 and of P2 (setting 1) or LSE2 - LSE1 - KL (setting 2), with log2 |g|
+  // folded into the exponent biases (g P = sign(g) 2^(y + log2 |g|)), and sign(g). Tiles whose g
+  // are all >= 0 (flag qneg = 0) never read the sign.
+  __shared__ __attribute__((aligned(16))) float qa[3][3][kBT];
+  __shared__ int qneg[3];
 
   int rank, slice;
   block_coords(s.bh, rank, slice);
@@ -1073,14 +1119,18 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dk[nb] = f32x16{};
 
-  BwdStage<D, 2> st;
-  // Per-query values of the prefetched tile, row threadIdx.x (< kBT, lanes of wave 0). They are
-  // only loaded here and turned into the tile's constants when the tile is staged, one tile of
-  // compute later, so that nothing waits for the loads in between.
+  const int a_base = col * 2 * D + 16 * (h ^ bwd_swz<D>(col));
+  int tb[2];
+  tr_bases<D>(l, tb);
+  DM dma;
+  dma.init(s.q_sr * 2);
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
+  // Per-query inputs of the next tile (wave 0, lanes 0..31, one query each), loaded into
+  // registers a tile before they are turned into that tile's constants, so that nothing waits
+  // for them in between.
   float rx1 = 0.f, rx2 = 0.f, rg = 0.f, rkl = 0.f;
   bool rvalid = false;
-  auto load_tile = [&](int t) {
-    st.load(Q1, Q2, s.q_sr, t * kBT, s.nq);
+  auto load_inputs = [&](int t) {
     if (threadIdx.x < kBT) {
       const int q = t * kBT + threadIdx.x;
       rvalid = q < s.nq;
@@ -1092,9 +1142,7 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
       }
     }
   };
-  auto stage_store = [&](int buf) {
-    uint16_t* base = lds + buf * BUF;
-    st.store(base, base + L::RM, base + 2 * L::RM, FREE);
+  auto make_constants = [&](int stg) {
     if (threadIdx.x < kBT) {
       // rows past n_q (and rows with g = 0) get P = 0: bias -inf
       float cq0 = -kInf, cq1 = SETTING == 1 ? -kInf : 0.f, cq2 = 1.f;
@@ -1105,63 +1153,61 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
         cq2 = rg < 0.f ? -1.f : 1.f;
       }
       const bool neg = __any(rvalid && rg < 0.f);
-      qa[buf][0][threadIdx.x] = cq0;
-      qa[buf][1][threadIdx.x] = cq1;
-      qa[buf][2][threadIdx.x] = cq2;
-      if (threadIdx.x == 0) qneg[buf] = neg ? 1 : 0;
+      qa[stg][0][threadIdx.x] = cq0;
+      qa[stg][1][threadIdx.x] = cq1;
+      qa[stg][2][threadIdx.x] = cq2;
+      if (threadIdx.x == 0) qneg[stg] = neg ? 1 : 0;
     }
   };
-  const int ntiles = t_hi >= t_lo ? t_hi - t_lo + 1 : 0;
-  if (ntiles > 0) {
-    load_tile(t_hi);
-    stage_store(0);
-    if (ntiles > 1) load_tile(t_hi - 1);
+  // Query tile t (Q1 and Q2 rows) into stage stg; rows past n_q read as 0. The compiler does not
+  // see these loads (inline assembly), so its own wait for the per-query inputs (vmcnt 0) also
+  // waits for them in wave 0: that wave keeps one tile of lead, the others two.
+  auto issue = [&](int t, int stg) {
+    dma.issue(Q1, Q2, s.q_sr, t * kBT, s.nq, lds0 + stg * DM::STAGE);
+  };
+  const int n = t_hi >= t_lo ? t_hi - t_lo + 1 : 0;
+  if (n > 0) issue(t_hi, 0);
+  if (n > 1) issue(t_hi - 1, 1);
+  if (n > 0) {
+    load_inputs(t_hi);
+    dma.wait(n > 1 ? 1 : 0);
+    make_constants(0);
+    if (n > 1) load_inputs(t_hi - 1);
   }
   __syncthreads();
 
-  for (int i = 0; i < ntiles; ++i) {
+  // one tile; the loop is unrolled three times so that the stage (i % 3) is a compile-time
+  // constant and every operand read is a per-lane register plus an immediate offset
+  auto tile = [&](int i, auto stgc) {
+    constexpr int STG = decltype(stgc)::value;
     const int t = t_hi - i;
-    const int buf = i & 1;
-    const uint16_t* base = lds + buf * BUF;
-    const uint16_t* qt1 = base;
-    const uint16_t* qt2 = base + L::RM;
-    const uint16_t* qtr = base + 2 * L::RM;
+    if (i + 2 < n) issue(t - 2, (STG + 2) % 3);
+    const unsigned char* stage = lds + STG * DM::STAGE;
+    const unsigned char* qt1 = stage;
+    const unsigned char* qt2 = stage + DM::TB;
+    const unsigned char* qtr = stage + FREE * DM::TB;
     const int qt0 = t * kBT;
     const bool skip = !wave_live || (CAUSAL && qt0 + kBT - 1 < kw0);
     if (!skip) {
-      f32x16 x1[kBwdRB], x2[kBwdRB];
-#pragma unroll
-      for (int rb = 0; rb < kBwdRB; ++rb) {
-        x1[rb] = f32x16{};
-        x2[rb] = f32x16{};
-      }
+      f32x16 x1 = f32x16{}, x2 = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        bf16x8 a1[kBwdRB], a2[kBwdRB];
-#pragma unroll
-        for (int rb = 0; rb < kBwdRB; ++rb) {
-          a1[rb] = lds_a_frag<D>(qt1, rb * 32 + col, kk, h);
-          a2[rb] = lds_a_frag<D>(qt2, rb * 32 + col, kk, h);
-        }
-#pragma unroll
-        for (int rb = 0; rb < kBwdRB; ++rb) {
-          x1[rb] = mfma(a1[rb], f1[kk], x1[rb]);
-          x2[rb] = mfma(a2[rb], f2[kk], x2[rb]);
-        }
+        x1 = mfma(swz_a_frag(qt1, a_base, kk), f1[kk], x1);
+        x2 = mfma(swz_a_frag(qt2, a_base, kk), f2[kk], x2);
       }
-      // dS^T of one 32-query block and its dK product; the element mask is compiled only into
+      // dS^T of the 32-query block and its dK product; the element mask is compiled only into
       // the variant used on tiles that straddle the diagonal or the ragged end
-      auto ds_block = [&](auto maskc, auto signc, int rb) {
+      auto ds_block = [&](auto maskc, auto signc) {
         constexpr bool MASK = decltype(maskc)::value;
         constexpr bool SIGNED = decltype(signc)::value;  // some g < 0 in this tile
         float ds[16];
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           // registers 4rq..4rq+3 hold 4 consecutive queries
-          const int qi = rb * 32 + rq * 8 + h * 4;
-          const float4 va0 = *reinterpret_cast<const float4*>(&qa[buf][0][qi]);
-          const float4 va1 = *reinterpret_cast<const float4*>(&qa[buf][1][qi]);
-          const float4 va2 = SIGNED ? *reinterpret_cast<const float4*>(&qa[buf][2][qi])
+          const int qi = rq * 8 + h * 4;
+          const float4 va0 = *reinterpret_cast<const float4*>(&qa[STG][0][qi]);
+          const float4 va1 = *reinterpret_cast<const float4*>(&qa[STG][1][qi]);
+          const float4 va2 = SIGNED ? *reinterpret_cast<const float4*>(&qa[STG][2][qi])
                                     : make_float4(1.f, 1.f, 1.f, 1.f);
           const float c0[4] = {va0.x, va0.y, va0.z, va0.w};
           const float c1[4] = {va1.x, va1.y, va1.z, va1.w};
@@ -1169,7 +1215,7 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int r = rq * 4 + j;
-            float e1 = x1[rb][r], e2 = x2[rb][r];
+            float e1 = x1[r], e2 = x2[r];
             const float d12 = e1 - e2;
             if (MASK) {
               const int q = qt0 + qi + j;
@@ -1192,27 +1238,32 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
           const bf16x8 a = pack8(ds + 8 * cc);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            dk[nb] = mfma(a, tr_frag(qtr, nb, rb * 2 + cc, col, h), dk[nb]);
+            dk[nb] = mfma(a, swz_tr_frag(qtr + cc * 32 * D, tb, nb), dk[nb]);
         }
       };
-      const bool signed_tile = qneg[buf] != 0;
-#pragma unroll
-      for (int rb = 0; rb < kBwdRB; ++rb) {
-        const int qb0 = qt0 + rb * 32;
-        const bool full = lane_flag((qb0 + 32 <= s.nq) && (!CAUSAL || qb0 >= kw0 + 31));
-        // two variants only (a third costs registers): tiles that straddle the diagonal or
-        // the ragged end, or hold a negative g, take the masked variant that applies the sign
-        if (full && !signed_tile)
-          ds_block(std::false_type{}, std::false_type{}, rb);
-        else
-          ds_block(std::true_type{}, std::true_type{}, rb);
-      }
+      const bool signed_tile = qneg[STG] != 0;
+      const bool full = lane_flag((qt0 + 32 <= s.nq) && (!CAUSAL || qt0 >= kw0 + 31));
+      // two variants only (a third costs registers): tiles that straddle the diagonal or the
+      // ragged end, or hold a negative g, take the masked variant that applies the sign
+      if (full && !signed_tile)
+        ds_block(std::false_type{}, std::false_type{});
+      else
+        ds_block(std::true_type{}, std::true_type{});
     }
-    if (i + 1 < ntiles) {
-      stage_store(buf ^ 1);
-      if (i + 2 < ntiles) load_tile(t - 2);
+    if (i + 1 < n) {
+      dma.wait(i + 2 < n ? 1 : 0);
+      make_constants((STG + 1) % 3);
+      if (i + 2 < n) load_inputs(t - 2);
     }
     __syncthreads();
+  };
+  for (int i = 0; i < n;) {
+    tile(i, std::integral_constant<int, 0>{});
+    if (++i >= n) break;
+    tile(i, std::integral_constant<int, 1>{});
+    if (++i >= n) break;
+    tile(i, std::integral_constant<int, 2>{});
+    ++i;
   }
   if (!wave_live) return;
   const long long obase = (long long)slice * s.nk;

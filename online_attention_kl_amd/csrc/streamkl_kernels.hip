@@ -1077,7 +1077,6 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   constexpr int BKW = 32 * kBwdWaves, KS = D / 16, NB = D / 32;
   constexpr int FREE = 2 - SETTING;  // tensor index of Q_free (side 2 for setting 1)
   using DM = BwdDma<D, 2>;
-  constexpr int NRAW = SETTING == 1 ? 3 : 4;  // per-query inputs: LSE1, LSE2, g (and KL)
   __shared__ __attribute__((aligned(16))) unsigned char lds[3 * DM::STAGE];
   // Per stage, the constants wave 0 makes from the tile's per-query inputs: per query the
   // exponent bias of P1 and of P2 (setting 1) or LSE2 - LSE1 - KL (setting 2), with log2 |g|

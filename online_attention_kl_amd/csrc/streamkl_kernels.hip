@@ -750,7 +750,8 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tr, int nb, int cc, in
 // ---------------------------------------------------------------- streamed tiles, direct to LDS
 // The backward kernels stream 32-row tiles of the other side's bf16 matrices. A tile goes from
 // global memory straight into LDS (buffer loads with an LDS destination: no registers and no LDS
-// store instructions), three stages deep, so a stage is loaded two tiles ahead of its use. Rows
+// store instructions), three stages deep: the loads of tile i + 2 are issued at the end of tile
+// i and land while tile i + 1 is computed. Rows
 // are unpadded (2 D bytes) and the 16-byte chunk c of row r sits at chunk position
 // c ^ bwd_swz(r). The permutation keeps both operand reads free of LDS bank conflicts: the 16-byte
 // row reads of the S recomputation (16 consecutive rows at one chunk per pass) and the 8-byte
@@ -963,7 +964,6 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   auto tile = [&](int i, auto stgc) {
     constexpr int STG = decltype(stgc)::value;
     const int t = t0 + i;
-    if (i + 2 < n) dma.issue(K1, K2, s.k_sr, (t + 2) * kBT, s.nk, lds0 + ((STG + 2) % 3) * DM::STAGE);
     const unsigned char* stage = lds + STG * DM::STAGE;
     const unsigned char* kt1 = stage;
     const unsigned char* kt2 = stage + (NTENS - 1) * DM::TB;
@@ -1014,6 +1014,10 @@ dq_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
       else
         ds_block(std::true_type{});
     }
+    // tile i + 2 into the stage tile i - 1 used (free since the last barrier), issued after this
+    // tile's operand reads so that its LDS writes do not meet them
+    if (i + 2 < n)
+      dma.issue(K1, K2, s.k_sr, (t + 2) * kBT, s.nk, lds0 + ((STG + 2) % 3) * DM::STAGE);
     if (i + 1 < n) dma.wait(i + 2 < n ? 1 : 0);
     __syncthreads();
   };
@@ -1160,7 +1164,7 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   };
   // Query tile t (Q1 and Q2 rows) into stage stg; rows past n_q read as 0. The compiler does not
   // see these loads (inline assembly), so its own wait for the per-query inputs (vmcnt 0) also
-  // waits for them in wave 0: that wave keeps one tile of lead, the others two.
+  // waits for them: the inputs are loaded after the tile and used a tile later, as the tile is.
   auto issue = [&](int t, int stg) {
     dma.issue(Q1, Q2, s.q_sr, t * kBT, s.nq, lds0 + stg * DM::STAGE);
   };
@@ -1180,7 +1184,6 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
   auto tile = [&](int i, auto stgc) {
     constexpr int STG = decltype(stgc)::value;
     const int t = t_hi - i;
-    if (i + 2 < n) issue(t - 2, (STG + 2) % 3);
     const unsigned char* stage = lds + STG * DM::STAGE;
     const unsigned char* qt1 = stage;
     const unsigned char* qt2 = stage + DM::TB;
@@ -1250,9 +1253,14 @@ dk_kernel(const uint16_t* __restrict__ q1, const uint16_t* __restrict__ k1,
         ds_block(std::true_type{}, std::true_type{});
     }
     if (i + 1 < n) {
-      dma.wait(i + 2 < n ? 1 : 0);
+      dma.wait(0);
       make_constants((STG + 1) % 3);
-      if (i + 2 < n) load_inputs(t - 2);
+    }
+    // tile i + 2 into the stage tile i - 1 used (free since the last barrier), issued after this
+    // tile's operand reads so that its LDS writes do not meet them, and after the wait above
+    if (i + 2 < n) {
+      issue(t - 2, (STG + 2) % 3);
+      load_inputs(t - 2);
     }
     __syncthreads();
   };

@@ -111,3 +111,26 @@ def test_mutated_swizzle_is_caught():
         addr.append((4 * h + e) * rb + 8 * (m & 1) + 16 * low)
     b = [x for a in addr for x in banks(a, 8)]
     assert len(set(b)) < len(b)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("ntens", [1, 2])
+def test_pieces_are_shared_out_once(d, ntens):
+    """Piece i of a stage (1 KB, tensor i // pieces-per-tensor) is loaded by wave i % 8 as its
+    load i // 8; every piece once, at most two loads per wave (what the wait before a barrier
+    allows for), and a wave's wait counts exactly the loads it issued."""
+    waves, tb = 8, 32 * 2 * d
+    ppt = tb // 1024
+    pieces = ntens * ppt
+    n = (pieces + waves - 1) // waves
+    assert n <= 2
+    seen = []
+    for w in range(waves):
+        cnt = 0
+        for j in range(n):
+            idx = w + j * waves
+            if idx < pieces:
+                seen.append((idx // ppt, idx % ppt))
+                cnt += 1
+        assert cnt == sum(1 for i in range(pieces) if i % waves == w)
+    assert sorted(seen) == [(te, p) for te in range(ntens) for p in range(ppt)]
